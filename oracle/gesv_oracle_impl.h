@@ -1,0 +1,247 @@
+/*
+ * Body of the CPU oracle, written once and included twice by gesv_oracle.c:
+ * once with REAL = double (suffix _f64) and once with REAL = float (suffix _f32).
+ * Every operation runs in REAL, the working precision of the system, because
+ * the pivot choice and the exact-zero test of the pivot are decisions taken in
+ * that precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  See gesv_oracle.c for the provenance of each step.
+ *
+ * Macros expected from the includer:
+ *   REAL   element type
+ *   SFX(x) appends the suffix (_f64 / _f32) to an identifier
+ *   FMA    fused multiply-add of REAL (fma / fmaf)
+ *   FABS   absolute value of REAL (fabs / fabsf)
+ */
+
+/* Logical element (r, c) of the matrix of one system, whatever its storage.
+ * Row-major: (r, c) at r*n + c.  Column-major: (r, c) at c*n + r. */
+static REAL SFX(load_a)(const REAL *a, int layout, int n, int r, int c)
+{
+    return layout == ORACLE_ROW_MAJOR ? a[(size_t)r * n + c] : a[(size_t)c * n + r];
+}
+
+/* Right-hand sides and solutions follow the same layout flag as the matrix:
+ * row-major n x nrhs (r, j) at r*nrhs + j, column-major at j*n + r. */
+static size_t SFX(rhs_index)(int layout, int n, int nrhs, int r, int j)
+{
+    return layout == ORACLE_ROW_MAJOR ? (size_t)r * nrhs + j : (size_t)j * n + r;
+}
+
+/*
+ * Partial pivoting, first maximum: scan the candidates of column k in
+ * increasing current row position, replacing the running choice only when a
+ * magnitude is strictly larger.  On equal magnitudes the lowest current
+ * position therefore wins (LAPACK's choice, the tie rule of the ruSOLVER
+ * numerical contract and the first-maximum rule of the SparseDirectSolver
+ * review).  Returns the position; *mag receives the winning magnitude.
+ */
+static int SFX(pivot_search)(const REAL *M, int n, int k, REAL *mag)
+{
+    int p = k;
+    REAL m = FABS(M[(size_t)k * n + k]);
+    for (int r = k + 1; r < n; ++r) {
+        REAL v = FABS(M[(size_t)r * n + k]);
+        if (v > m) {
+            p = r;
+            m = v;
+        }
+    }
+    *mag = m;
+    return p;
+}
+
+static void SFX(swap_rows)(REAL *M, int width, int i, int j)
+{
+    for (int c = 0; c < width; ++c) {
+        REAL t = M[(size_t)i * width + c];
+        M[(size_t)i * width + c] = M[(size_t)j * width + c];
+        M[(size_t)j * width + c] = t;
+    }
+}
+
+/*
+ * gesv of one system.  M (n*n) and Y (n*nrhs) are scratch, logical row-major.
+ *
+ * Right-looking LU with partial row pivoting, P A = L U, with the forward
+ * substitution L y = P b carried along with the elimination (each rank-1
+ * step also updates the right-hand sides), then U x = y by back substitution
+ * taken one solution entry at a time, that entry then eliminated from the
+ * rows above it.  This is the order of the cooperative LU solver page
+ * (solver_static.hpp, Detailed Description, column-major case) and of its
+ * "Departures from the MAGMA kernel" (solution entry kept by its owner).
+ *
+ * Result contract (ruSOLVER small-matrix page, section on the unchanged
+ * numerical and failure contract): status 0 on success, k >= 1 for the
+ * first pivot that fails (here: an exactly zero pivot, 1-based step); a
+ * failed system has every solution entry +0.0 and every pivot -1.
+ */
+static int SFX(gesv_one)(int layout, int n, int nrhs, const REAL *a, const REAL *b,
+                         REAL *x, int32_t *piv, REAL *M, REAL *Y)
+{
+    for (int r = 0; r < n; ++r)
+        for (int c = 0; c < n; ++c)
+            M[(size_t)r * n + c] = SFX(load_a)(a, layout, n, r, c);
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)r * nrhs + j] = b[SFX(rhs_index)(layout, n, nrhs, r, j)];
+
+    int info = 0;
+    for (int k = 0; k < n; ++k) {
+        REAL mag;
+        int p = SFX(pivot_search)(M, n, k, &mag);
+        piv[k] = p;
+        if (mag == 0) { /* exactly zero pivot: the first failure decides */
+            info = k + 1;
+            break;
+        }
+        if (p != k) {
+            SFX(swap_rows)(M, n, k, p);
+            SFX(swap_rows)(Y, nrhs, k, p);
+        }
+        const REAL d = M[(size_t)k * n + k];
+        for (int r = k + 1; r < n; ++r) {
+            /* multiplier by correctly rounded IEEE division (no reciprocal) */
+            const REAL l = M[(size_t)r * n + k] / d;
+            M[(size_t)r * n + k] = l;
+            for (int c = k + 1; c < n; ++c)
+                M[(size_t)r * n + c] = FMA(-l, M[(size_t)k * n + c], M[(size_t)r * n + c]);
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)r * nrhs + j] = FMA(-l, Y[(size_t)k * nrhs + j], Y[(size_t)r * nrhs + j]);
+        }
+    }
+
+    if (info != 0) {
+        for (int r = 0; r < n; ++r) {
+            piv[r] = -1;
+            for (int j = 0; j < nrhs; ++j)
+                x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;
+        }
+        return info;
+    }
+
+    /* U x = y: x_k = y_k / u_kk, then x_k leaves the rows r < k. */
+    for (int k = n - 1; k >= 0; --k) {
+        const REAL ukk = M[(size_t)k * n + k];
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / ukk;
+        for (int r = 0; r < k; ++r)
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)r * nrhs + j] =
+                    FMA(-M[(size_t)r * n + k], Y[(size_t)k * nrhs + j], Y[(size_t)r * nrhs + j]);
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            x[SFX(rhs_index)(layout, n, nrhs, r, j)] = Y[(size_t)r * nrhs + j];
+    return 0;
+}
+
+/*
+ * getrf of one system: the same elimination, but it records the factors and
+ * does not stop at a zero pivot, so that P A = L U can be rebuilt for every
+ * input (a zero pivot column gets zero multipliers: all its candidates are
+ * zero already).  lu (n*n, logical row-major) receives L strictly below the
+ * diagonal (unit diagonal implied) and U on and above it, in LAPACK's
+ * pivoted row order; ipiv[k] is the 0-based position swapped with k at step k.
+ *
+ * *gap receives the smallest, over the steps k <= n-2, relative distance
+ * (|c1| - |c2|) / |c1| between the two largest candidate magnitudes of the
+ * step (0 when the largest is 0; 1 when n == 1).  A small gap marks a pivot
+ * choice that rounding could flip.
+ */
+static int SFX(getrf_one)(int layout, int n, const REAL *a, REAL *lu, int32_t *ipiv, double *gap)
+{
+    for (int r = 0; r < n; ++r)
+        for (int c = 0; c < n; ++c)
+            lu[(size_t)r * n + c] = SFX(load_a)(a, layout, n, r, c);
+
+    int info = 0;
+    double g = 1.0;
+    for (int k = 0; k < n; ++k) {
+        REAL mag;
+        int p = SFX(pivot_search)(lu, n, k, &mag);
+        ipiv[k] = p;
+        if (k <= n - 2) {
+            /* second largest candidate magnitude of column k */
+            REAL second = 0;
+            for (int r = k; r < n; ++r) {
+                if (r == p)
+                    continue;
+                REAL v = FABS(lu[(size_t)r * n + k]);
+                if (v > second)
+                    second = v;
+            }
+            double gk = mag == 0 ? 0.0 : ((double)mag - (double)second) / (double)mag;
+            if (gk < g)
+                g = gk;
+        }
+        if (mag == 0) {
+            if (info == 0)
+                info = k + 1;
+            for (int r = k + 1; r < n; ++r)
+                lu[(size_t)r * n + k] = 0;
+            continue;
+        }
+        if (p != k)
+            SFX(swap_rows)(lu, n, k, p);
+        const REAL d = lu[(size_t)k * n + k];
+        for (int r = k + 1; r < n; ++r) {
+            const REAL l = lu[(size_t)r * n + k] / d;
+            lu[(size_t)r * n + k] = l;
+            for (int c = k + 1; c < n; ++c)
+                lu[(size_t)r * n + c] = FMA(-l, lu[(size_t)k * n + c], lu[(size_t)r * n + c]);
+        }
+    }
+    *gap = g;
+    return info;
+}
+
+int SFX(oracle_gesv)(int layout, int n, int nrhs, int64_t batch, const REAL *A, const REAL *B,
+                     REAL *X, int32_t *piv, int32_t *info, int nthreads)
+{
+    int rc = oracle_check_args(layout, n, nrhs, batch);
+    if (rc != 0)
+        return rc;
+    if (batch == 0)
+        return 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        REAL *M = (REAL *)malloc(sizeof(REAL) * (size_t)n * n);
+        REAL *Y = (REAL *)malloc(sizeof(REAL) * (size_t)n * nrhs);
+        if (M == NULL || Y == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t s = 0; s < batch; ++s) {
+                info[s] = SFX(gesv_one)(layout, n, nrhs, A + s * (int64_t)n * n,
+                                        B + s * (int64_t)n * nrhs, X + s * (int64_t)n * nrhs,
+                                        piv + s * (int64_t)n, M, Y);
+            }
+        }
+        free(M);
+        free(Y);
+    }
+    return failed ? ORACLE_ENOMEM : 0;
+}
+
+int SFX(oracle_getrf)(int layout, int n, int64_t batch, const REAL *A, REAL *LU, int32_t *ipiv,
+                      int32_t *info, double *gap, int nthreads)
+{
+    int rc = oracle_check_args(layout, n, 1, batch);
+    if (rc != 0)
+        return rc;
+    if (batch == 0)
+        return 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t s = 0; s < batch; ++s) {
+        info[s] = SFX(getrf_one)(layout, n, A + s * (int64_t)n * n, LU + s * (int64_t)n * n,
+                                 ipiv + s * (int64_t)n, gap + s);
+    }
+    return 0;
+}

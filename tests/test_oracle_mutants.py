@@ -1,0 +1,92 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case copies the oracle's C source, plants one mistake by a text
+substitution (a flipped sign, a transposed index, a dropped term, a changed
+tie rule, ...), builds the copy with the same compiler flags and runs a fast
+selection of the pins against it: at least one must fail.  The unmodified
+copy must pass the same selection.  Everything here runs on the CPU.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC_DIR = os.path.dirname(oracle.__file__)
+IMPL = "gesv_oracle_impl.h"
+
+MUTANTS = {
+    "update_sign": ("FMA(-l, M[(size_t)k * n + c], M[(size_t)r * n + c])",
+                    "FMA(l, M[(size_t)k * n + c], M[(size_t)r * n + c])"),
+    "update_transposed": ("FMA(-l, M[(size_t)k * n + c], M[(size_t)r * n + c])",
+                          "FMA(-l, M[(size_t)c * n + k], M[(size_t)r * n + c])"),
+    "rhs_update_dropped": ("Y[(size_t)r * nrhs + j] = FMA(-l, Y[(size_t)k * nrhs + j], "
+                           "Y[(size_t)r * nrhs + j]);",
+                           "(void)0;"),
+    "rhs_swap_dropped": ("SFX(swap_rows)(Y, nrhs, k, p);", "(void)0;"),
+    "tie_to_last": ("if (v > m) {", "if (v >= m) {"),
+    "candidate_skipped": ("for (int r = k + 1; r < n; ++r) {\n        REAL v = FABS",
+                          "for (int r = k + 2; r < n; ++r) {\n        REAL v = FABS"),
+    "reciprocal_multiplier": ("const REAL l = M[(size_t)r * n + k] / d;",
+                              "const REAL l = M[(size_t)r * n + k] * ((REAL)1 / d);"),
+    "backsub_transposed": ("FMA(-M[(size_t)r * n + k], Y[(size_t)k * nrhs + j]",
+                           "FMA(-M[(size_t)k * n + r], Y[(size_t)k * nrhs + j]"),
+    "backsub_no_division": ("Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / ukk;",
+                            "Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j];"),
+    "colmajor_as_rowmajor": ("? a[(size_t)r * n + c] : a[(size_t)c * n + r]",
+                             "? a[(size_t)r * n + c] : a[(size_t)r * n + c]"),
+    "info_zero_based": ("info = k + 1;\n            break;", "info = k;\n            break;"),
+    "failed_piv_kept": ("piv[r] = -1;", "(void)0;"),
+    "lu_multiplier_not_stored": ("lu[(size_t)r * n + k] = l;\n", "(void)l;\n"),
+}
+
+
+def _selection():
+    """A fast subset of the pins, enough to cover every step."""
+    yield lambda: pins.test_golden_examples(np.float64, "row", None)
+    yield lambda: pins.test_golden_examples(np.float32, "col", 8)
+    yield lambda: pins.test_lapack_pivots(np.float64, "row")
+    yield lambda: pins.test_lapack_pivots(np.float32, "col")
+    yield lambda: pins.test_reconstruction_bound(np.float64, "row")
+    yield lambda: pins.test_exact_singularity_constructions(np.float64, "row")
+    yield lambda: pins.test_exact_singularity_constructions(np.float32, "col")
+    yield lambda: pins.test_cramer_exact(np.float64, "col", 3)
+
+
+def _build_variant(tmp_path, name, mutation):
+    d = tmp_path / name
+    d.mkdir()
+    for f in ("gesv_oracle.c", IMPL):
+        shutil.copy(os.path.join(SRC_DIR, f), d / f)
+    if mutation is not None:
+        old, new = mutation
+        text = (d / IMPL).read_text(encoding="utf-8")
+        assert text.count(old) >= 1, f"mutation site of {name} not found"
+        (d / IMPL).write_text(text.replace(old, new, 1), encoding="utf-8")
+    return oracle.build(source_dir=str(d), out=str(d / "lib.so"))
+
+
+def _failures(lib_path):
+    failed = []
+    with oracle.use_library(lib_path):
+        for i, check in enumerate(_selection()):
+            try:
+                check()
+            except AssertionError:
+                failed.append(i)
+    return failed
+
+
+def test_unmodified_copy_passes(tmp_path):
+    assert _failures(_build_variant(tmp_path, "control", None)) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    failed = _failures(_build_variant(tmp_path, name, MUTANTS[name]))
+    assert failed, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,420 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test ties the oracle to something it cannot reproduce by itself being
+wrong in the same way: hand-worked examples, exact rational arithmetic
+(Cramer's rule, exact Gaussian elimination), the textbook backward-error
+bound of LU factorization, LAPACK's pivot sequence, closed forms of special
+matrices and exact-singularity constructions.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import golden_io
+import metrics
+import oracle
+
+DTYPES = [np.float64, np.float32]
+LAYOUTS = ["row", "col"]
+
+
+def _solve_logical(A, B, dtype, layout, nthreads=0):
+    """Run the oracle on logical A [batch,n,n], B [batch,n,nrhs]."""
+    A = np.asarray(A, dtype=dtype)
+    B = np.asarray(B, dtype=dtype)
+    n, nrhs = A.shape[1], B.shape[2]
+    X_st, piv, info = oracle.gesv(oracle.to_storage(A, layout), oracle.rhs_to_storage(B, layout),
+                                  n, nrhs, layout, nthreads)
+    return oracle.rhs_from_storage(X_st, layout, n, nrhs), piv, info
+
+
+def _factor_logical(A, dtype, layout):
+    A = np.asarray(A, dtype=dtype)
+    return oracle.getrf(oracle.to_storage(A, layout), A.shape[1], layout)
+
+
+# ---------------------------------------------------------------- hand-worked
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("embed", [None, 8])
+def test_golden_examples(dtype, layout, embed):
+    for ex in golden_io.all_examples():
+        if embed:
+            ex = golden_io.embed_identity(ex, embed)
+        A = ex["A"][None]
+        b = ex["b"][None, :, None]
+        X, piv, info = _solve_logical(A, b, dtype, layout)
+        assert info[0] == ex["info"], ex["name"]
+        np.testing.assert_array_equal(piv[0], ex["piv"], err_msg=ex["name"])
+        # every value of these examples is a dyadic rational: exact equality
+        np.testing.assert_array_equal(X[0, :, 0], ex["x"].astype(dtype), err_msg=ex["name"])
+        if ex["info"] != 0:
+            assert not np.signbit(X).any(), "failed system must hold +0.0"
+        LU, ipiv, ginfo, _ = _factor_logical(A, dtype, layout)
+        np.testing.assert_array_equal(ipiv[0], ex["ipiv"], err_msg=ex["name"])
+        assert ginfo[0] == ex["getrf_info"]
+        if "L" in ex:
+            L = np.tril(LU[0], -1) + np.eye(3)
+            U = np.triu(LU[0])
+            np.testing.assert_array_equal(L, ex["L"].astype(dtype))
+            np.testing.assert_array_equal(U, ex["U"].astype(dtype))
+
+
+# ------------------------------------------------------ exact rational pins
+
+
+def _det(M):
+    """Exact determinant by cofactor expansion (n <= 4)."""
+    n = len(M)
+    if n == 1:
+        return M[0][0]
+    if n == 2:
+        return M[0][0] * M[1][1] - M[0][1] * M[1][0]
+    total = Fraction(0)
+    for c in range(n):
+        minor = [row[:c] + row[c + 1:] for row in M[1:]]
+        total += (-1) ** c * M[0][c] * _det(minor)
+    return total
+
+
+def _cramer(A, b):
+    n = len(A)
+    M = [[Fraction(float(v)) for v in row] for row in A]
+    bb = [Fraction(float(v)) for v in b]
+    d = _det(M)
+    if d == 0:
+        return None
+    x = []
+    for i in range(n):
+        Mi = [row[:i] + [bb[r]] + row[i + 1:] for r, row in enumerate(M)]
+        x.append(_det(Mi) / d)
+    return x
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_cramer_exact(dtype, layout, n):
+    """Solution vs Cramer's rule in exact rationals from the exact inputs.
+
+    Bound: the computed x solves (A + dA) x = b with |dA| <= gamma_3n |L||U|
+    (backward error of Gaussian elimination), |L||U| <= n * 2**(n-1) |A| in
+    norm under partial pivoting, so the forward error is at most
+    kappa * gamma_3n * n * 2**(n-1) / (1 - that)."""
+    rng = np.random.default_rng(100 + n)
+    batch = 300
+    A = rng.uniform(-1, 1, size=(batch, n, n)).astype(dtype)
+    B = rng.uniform(-1, 1, size=(batch, n, 2)).astype(dtype)
+    X, piv, info = _solve_logical(A, B, dtype, layout)
+    u = metrics.UNIT_ROUNDOFF[np.dtype(dtype)]
+    kappa = metrics.kappa_inf(A.astype(np.float64))
+    gamma = 3 * n * u / (1 - 3 * n * u)
+    checked = 0
+    for s in range(batch):
+        if not np.isfinite(kappa[s]) or kappa[s] > 1e6:
+            continue
+        assert info[s] == 0
+        f = kappa[s] * gamma * n * 2 ** (n - 1)
+        bound = f / (1 - f)
+        for j in range(2):
+            xs = _cramer(A[s], B[s, :, j])
+            xs_f = np.array([float(v) for v in xs])
+            err = np.abs(X[s, :, j].astype(np.float64) - xs_f).max() / np.abs(xs_f).max()
+            assert err <= bound, (s, j, err, bound)
+        checked += 1
+    assert checked > batch // 2
+
+
+def _exact_gepp(A):
+    """Gaussian elimination with partial pivoting in exact rationals, first
+    maximum in increasing current position.  Returns (ipiv, singular_step)."""
+    n = len(A)
+    M = [[Fraction(float(v)) for v in row] for row in A]
+    ipiv = []
+    first_zero = 0
+    for k in range(n):
+        p = k
+        for r in range(k + 1, n):
+            if abs(M[r][k]) > abs(M[p][k]):
+                p = r
+        ipiv.append(p)
+        if M[p][k] == 0:
+            if first_zero == 0:
+                first_zero = k + 1
+            continue
+        M[k], M[p] = M[p], M[k]
+        for r in range(k + 1, n):
+            l = M[r][k] / M[k][k]
+            for c in range(k, n):
+                M[r][c] -= l * M[k][c]
+    return ipiv, first_zero
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n", [2, 3, 5, 6])
+def test_exact_gepp_pivots(dtype, n):
+    """Pivot sequence vs exact-rational elimination on inputs whose float
+    pivot gap is comfortable (rounding cannot flip the choice there)."""
+    rng = np.random.default_rng(7 + n)
+    A = rng.uniform(-1, 1, size=(200, n, n)).astype(dtype)
+    _, ipiv, info, gap = _factor_logical(A, dtype, "row")
+    checked = 0
+    for s in range(A.shape[0]):
+        if gap[s] < 1e-3:
+            continue
+        ex_piv, ex_zero = _exact_gepp(A[s])
+        np.testing.assert_array_equal(ipiv[s], ex_piv)
+        assert info[s] == ex_zero
+        checked += 1
+    assert checked > 100
+
+
+def test_exact_gepp_integer_ties():
+    """Small-integer matrices have many exact magnitude ties; whenever every
+    float step is exact (checked by comparing against the rational run),
+    the tie decisions must agree with exact elimination."""
+    rng = np.random.default_rng(3)
+    agree = 0
+    for _ in range(400):
+        n = int(rng.integers(2, 6))
+        A = rng.integers(-2, 3, size=(n, n)).astype(np.float64)
+        ex_piv, ex_zero = _exact_gepp(A)
+        LU, ipiv, info, _ = _factor_logical(A[None], np.float64, "row")
+        if ex_zero == 0 and np.isfinite(LU).all():
+            # exact rational factors, rounded: if they are representable the
+            # float run followed the exact one step by step
+            P = metrics.apply_swaps(A[None], np.array([ex_piv]))[0]
+            L = np.tril(LU[0], -1) + np.eye(n)
+            U = np.triu(LU[0])
+            if np.array_equal(L @ U, P):
+                np.testing.assert_array_equal(ipiv[0], ex_piv)
+                agree += 1
+    assert agree > 100
+
+
+# ----------------------------------------------------- factorization bound
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_reconstruction_bound(dtype, layout):
+    """|P A - L U| <= gamma_n |L| |U| componentwise (backward error of the
+    computed LU factors), and |L_ij| <= 1 (partial pivoting), for random n in
+    [1, 64] and several value distributions."""
+    rng = np.random.default_rng(11)
+    u = metrics.UNIT_ROUNDOFF[np.dtype(dtype)]
+    for trial in range(40):
+        n = int(rng.integers(1, 65))
+        kind = trial % 4
+        if kind == 0:
+            A = rng.uniform(-1, 1, size=(3, n, n))
+        elif kind == 1:
+            A = rng.standard_normal(size=(3, n, n)) + 0.5 * np.eye(n)
+        elif kind == 2:
+            A = rng.uniform(-1, 1, size=(3, n, n)) * 10.0 ** rng.uniform(-3, 3, size=(3, n, 1))
+        else:
+            A = rng.standard_normal(size=(3, n, n)) * 10.0 ** rng.uniform(-3, 3, size=(3, 1, n))
+        A = A.astype(dtype)
+        LU, ipiv, info, _ = _factor_logical(A, dtype, layout)
+        gamma = n * u / (1 - n * u)
+        for s in range(A.shape[0]):
+            L = (np.tril(LU[s], -1) + np.eye(n)).astype(np.longdouble)
+            U = np.triu(LU[s]).astype(np.longdouble)
+            PA = metrics.apply_swaps(A[s][None].astype(np.longdouble), ipiv[s][None])[0]
+            diff = np.abs(PA - L @ U)
+            bound = gamma * (np.abs(L) @ np.abs(U))
+            # the extended-precision product adds at most n * 2**-64 relative
+            slack = n * 2.0 ** -63 * (np.abs(L) @ np.abs(U))
+            assert (diff <= bound + slack).all(), (n, trial, s)
+            assert (np.abs(np.tril(LU[s], -1)) <= 1).all()
+
+
+# ------------------------------------------------------------ LAPACK pivots
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_lapack_pivots(dtype, layout):
+    """ipiv equals LAPACK getrf's (scipy lu_factor, 0-based) on inputs whose
+    pivot gap leaves no room for rounding to flip a choice; U agrees within
+    rounding; the solution agrees with LAPACK gesv within kappa-scaled bounds."""
+    rng = np.random.default_rng(5)
+    thr = 1e-9 if dtype == np.float64 else 1e-4
+    u = metrics.UNIT_ROUNDOFF[np.dtype(dtype)]
+    checked = 0
+    for trial in range(60):
+        n = int(rng.integers(1, 65))
+        A = rng.standard_normal(size=(4, n, n)).astype(dtype)
+        B = rng.standard_normal(size=(4, n, 3)).astype(dtype)
+        LU, ipiv, info, gap = _factor_logical(A, dtype, layout)
+        X, piv, sinfo = _solve_logical(A, B, dtype, layout)
+        for s in range(A.shape[0]):
+            if gap[s] < thr:
+                continue
+            lu, lpiv = scipy.linalg.lu_factor(A[s], check_finite=False)
+            np.testing.assert_array_equal(ipiv[s], lpiv.astype(np.int32))
+            np.testing.assert_array_equal(piv[s], lpiv.astype(np.int32))
+            assert info[s] == 0 and sinfo[s] == 0
+            scale = np.abs(np.triu(lu)).max()
+            assert np.abs(np.triu(LU[s]) - np.triu(lu)).max() <= 64 * n * u * scale * 10
+            xl = scipy.linalg.lu_solve((lu, lpiv), B[s], check_finite=False)
+            kap = metrics.kappa_inf(A[s][None].astype(np.float64))[0]
+            err = np.abs(X[s] - xl).max() / np.abs(xl).max()
+            assert err <= 8 * n * n * u * kap + 1e-300, (n, err)
+            checked += 1
+    assert checked > 150
+
+
+# ---------------------------------------------------------- special cases
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_special_matrices(dtype, layout):
+    rng = np.random.default_rng(21)
+    for n in (1, 2, 7, 8, 16, 24, 33, 64):
+        nrhs = 3
+        B = rng.uniform(-1, 1, size=(1, n, nrhs)).astype(dtype)
+        # identity: x = b, no swaps
+        X, piv, info = _solve_logical(np.eye(n)[None], B, dtype, layout)
+        np.testing.assert_array_equal(X, B)
+        np.testing.assert_array_equal(piv[0], np.arange(n))
+        assert info[0] == 0
+        # permutation matrix P (A[i, perm[i]] = 1): x[perm[i]] = b[i], exactly
+        perm = rng.permutation(n)
+        P = np.zeros((n, n))
+        P[np.arange(n), perm] = 1
+        X, piv, info = _solve_logical(P[None], B, dtype, layout)
+        expect = np.empty_like(B[0])
+        expect[perm] = B[0]
+        np.testing.assert_array_equal(X[0], expect)
+        assert info[0] == 0
+        # diagonal: x = b / d correctly rounded
+        d = rng.uniform(0.5, 2.0, size=n) * rng.choice([-1, 1], size=n)
+        D = np.diag(d).astype(dtype)
+        X, piv, info = _solve_logical(D[None], B, dtype, layout)
+        np.testing.assert_array_equal(X[0], B[0] / d.astype(dtype)[:, None])
+        np.testing.assert_array_equal(piv[0], np.arange(n))
+        # upper triangular with a non-zero diagonal: no swap
+        Uu = np.triu(rng.uniform(-1, 1, size=(n, n))) + np.diag(rng.uniform(1, 2, size=n))
+        X, piv, info = _solve_logical(Uu[None], B, dtype, layout)
+        np.testing.assert_array_equal(piv[0], np.arange(n))
+        assert info[0] == 0
+        # x = U^-1 b by the same back substitution order -> scipy agrees closely
+        xs = scipy.linalg.solve_triangular(Uu.astype(dtype), B[0])
+        assert np.abs(X[0] - xs).max() <= 1e3 * n * metrics.EPS[np.dtype(dtype)] * np.abs(xs).max()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_power_of_two_scaling(dtype, layout):
+    """A * 2**j gives the same pivots and x * 2**-j bit for bit (power-of-two
+    scaling is exact, so every multiplier is unchanged)."""
+    rng = np.random.default_rng(8)
+    A = rng.standard_normal(size=(50, 20, 20)).astype(dtype)
+    B = rng.standard_normal(size=(50, 20, 2)).astype(dtype)
+    X0, piv0, info0 = _solve_logical(A, B, dtype, layout)
+    for j in (-7, 3, 11):
+        X1, piv1, info1 = _solve_logical(A * dtype(2.0 ** j), B, dtype, layout)
+        np.testing.assert_array_equal(piv1, piv0)
+        np.testing.assert_array_equal(info1, info0)
+        np.testing.assert_array_equal(X1, X0 * dtype(2.0 ** -j))
+
+
+# ------------------------------------------------------------ singularity
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_exact_singularity_constructions(dtype, layout):
+    """Constructions whose first zero pivot is known exactly.
+
+    * two bitwise-equal rows: while neither is the pivot both receive the
+      same updates; once one is the pivot the other gets the multiplier 1
+      (exact quotient) and becomes exactly zero, a zero row that can only be
+      the last pivot -> status n.
+    * a zero row -> status n.  * zero column j -> status j+1.
+    * zero matrix -> status 1."""
+    rng = np.random.default_rng(13)
+    for n in (2, 3, 8, 16, 24, 32, 64):
+        batch = 40
+        A = rng.uniform(-1, 1, size=(batch, n, n)).astype(dtype)
+        B = rng.uniform(-1, 1, size=(batch, n, 1)).astype(dtype)
+        for s in range(batch):
+            i, k = rng.choice(n, size=2, replace=False)
+            A[s, k] = A[s, i]
+        X, piv, info = _solve_logical(A, B, dtype, layout)
+        assert (info == n).all(), (n, info)
+        assert (piv == -1).all() and (X == 0).all() and not np.signbit(X).any()
+        # zero row
+        A = rng.uniform(-1, 1, size=(batch, n, n)).astype(dtype)
+        A[np.arange(batch), rng.integers(0, n, size=batch)] = 0
+        _, _, info = _solve_logical(A, B, dtype, layout)
+        assert (info == n).all()
+        # zero column j
+        A = rng.uniform(-1, 1, size=(batch, n, n)).astype(dtype)
+        cols = rng.integers(0, n, size=batch)
+        A[np.arange(batch), :, cols] = 0
+        _, _, info = _solve_logical(A, B, dtype, layout)
+        np.testing.assert_array_equal(info, cols + 1)
+        # zero matrix
+        _, piv, info = _solve_logical(np.zeros((1, n, n)), B[:1], dtype, layout)
+        assert info[0] == 1 and (piv == -1).all()
+
+
+# -------------------------------------------------------------- pivot gap
+
+
+def test_pivot_gap_values():
+    """Gap of hand-built columns: first column (4, 3, -1) -> (4-3)/4; later
+    steps of an upper-triangular matrix have one non-zero candidate -> 1."""
+    A = np.array([[[4.0, 0, 0], [3.0, 1, 0], [-1.0, 0, 1]]])
+    _, _, _, gap = oracle.getrf(oracle.to_storage(A, "row"), 3, "row")
+    # step 0: (4-3)/4 = 0.25.  step 1: after l = 0.75, -0.25 the column 1
+    # candidates are 1 and 0 -> gap 1.
+    assert gap[0] == 0.25
+    T = np.triu(np.ones((5, 5))) * 2
+    _, _, _, gap = oracle.getrf(oracle.to_storage(T[None], "row"), 5, "row")
+    assert gap[0] == 1.0
+    Z = np.array([[[1.0, 2.0], [-1.0, 5.0]]])
+    _, _, _, gap = oracle.getrf(oracle.to_storage(Z, "row"), 2, "row")
+    assert gap[0] == 0.0
+
+
+# ------------------------------------------------------------- layouts
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_layouts_bitwise_equal(dtype):
+    """The layout flag only changes addressing: the same logical system gives
+    identical bits in both layouts (and each layout is pinned by the tests
+    above against facts about the logical matrix)."""
+    rng = np.random.default_rng(17)
+    A = rng.standard_normal(size=(64, 24, 24)).astype(dtype)
+    B = rng.standard_normal(size=(64, 24, 3)).astype(dtype)
+    Xr, pr, ir = _solve_logical(A, B, dtype, "row")
+    Xc, pc, ic = _solve_logical(A, B, dtype, "col")
+    np.testing.assert_array_equal(Xr, Xc)
+    np.testing.assert_array_equal(pr, pc)
+    np.testing.assert_array_equal(ir, ic)
+
+
+def test_threads_do_not_change_results():
+    rng = np.random.default_rng(19)
+    A = rng.standard_normal(size=(257, 16, 16))
+    B = rng.standard_normal(size=(257, 16, 4))
+    X1, p1, i1 = _solve_logical(A, B, np.float64, "row", nthreads=1)
+    X4, p4, i4 = _solve_logical(A, B, np.float64, "row", nthreads=4)
+    np.testing.assert_array_equal(X1, X4)
+    np.testing.assert_array_equal(p1, p4)
+
+
+def test_empty_batch():
+    X, piv, info = oracle.gesv(np.zeros((0,)), np.zeros((0,)), 8, 1, "row")
+    assert X.size == 0 and piv.shape == (0, 8) and info.shape == (0,)

@@ -1,0 +1,91 @@
+"""The seeded input recipes (CPU only)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_linear_solvers_amd import workloads
+
+
+@pytest.mark.parametrize("name", sorted(workloads.RECIPES))
+def test_shapes_and_determinism(name):
+    r = workloads.RECIPES[name]
+    w1 = workloads.make(name, seed=0, batch=300)
+    w2 = workloads.make(name, seed=0, batch=300)
+    dt = np.float32 if r.dtype == "f32" else np.float64
+    assert w1.A.dtype == dt and w1.B.dtype == dt
+    assert w1.A.shape == (300, r.n, r.n)
+    assert w1.B.shape == ((300, r.n, r.nrhs) if r.layout == "row" else (300, r.nrhs, r.n))
+    assert w1.A.flags.c_contiguous and w1.B.flags.c_contiguous
+    np.testing.assert_array_equal(w1.A, w2.A)
+    np.testing.assert_array_equal(w1.B, w2.B)
+    w3 = workloads.make(name, seed=1, batch=300)
+    assert not np.array_equal(w1.A, w3.A)
+
+
+def test_chunked_draws_match_one_draw():
+    for dist in ("uniform", "normal"):
+        g1 = np.random.default_rng(4)
+        g2 = np.random.default_rng(4)
+        a = workloads._draw(g1, dist, (1000, 5, 5), chunk_rows=64)
+        b = (g2.uniform(-1, 1, size=(1000, 5, 5)) if dist == "uniform"
+             else g2.standard_normal(size=(1000, 5, 5)))
+        np.testing.assert_array_equal(a, b)
+
+
+def test_singular_recipe():
+    w = workloads.make("n16_f32_row_sing", batch=2000)
+    sing = w.meta["singular"]
+    assert sing.size == 20 and np.unique(sing).size == 20
+    np.testing.assert_array_equal(w.A[sing, 5, :], w.A[sing, 0, :])
+    others = np.setdiff1d(np.arange(2000), sing)
+    assert not (w.A[others, 5, :] == w.A[others, 0, :]).all(axis=1).any()
+
+
+def test_row_scaled_recipe():
+    w = workloads.make("n24_f32_row_scl", batch=500)
+    rowmax = np.abs(w.A.astype(np.float64)).max(axis=2)
+    assert rowmax.max() > 100 and rowmax.min() < 0.01
+    assert np.abs(w.B).max() <= 1
+
+
+def test_shifted_recipe_diagonal():
+    w0 = workloads.make("n64_f64_row", batch=400)
+    d = np.diagonal(w0.A, axis1=1, axis2=2)
+    off = w0.A[:, 0, 1:]
+    assert abs(d.mean() - 0.5) < 0.05 and abs(off.mean()) < 0.05
+
+
+def test_column_major_storage():
+    w = workloads.make("n32_f64_col", batch=50)
+    rng = np.random.default_rng(0)
+    A = rng.standard_normal(size=(50, 32, 32))
+    B = rng.standard_normal(size=(50, 32, 1))
+    np.testing.assert_array_equal(w.A, A.transpose(0, 2, 1))
+    np.testing.assert_array_equal(w.B, B.transpose(0, 2, 1))
+    assert w.meta["gap_filtered"] is False
+
+
+def test_gap_redraw_uses_given_function():
+    calls = []
+
+    def fake_gap(A_st, n, layout):
+        calls.append(A_st.shape[0])
+        g = np.ones(A_st.shape[0])
+        if len(calls) == 1:
+            g[[3, 7]] = 0.0
+        return g
+
+    base = workloads.make("n32_f64_col", batch=20)
+    w = workloads.make("n32_f64_col", batch=20, gap_fn=fake_gap)
+    assert calls == [20, 2] and w.meta["redrawn"] == 2
+    keep = np.setdiff1d(np.arange(20), [3, 7])
+    np.testing.assert_array_equal(w.A[keep], base.A[keep])
+    assert not np.array_equal(w.A[3], base.A[3])
+
+
+def test_gap_redraw_with_oracle():
+    w = workloads.make("n32_f64_col", batch=3000, gap_fn=oracle.pivot_gap)
+    assert w.meta["gap_filtered"]
+    assert (oracle.pivot_gap(w.A, 32, "col") >= workloads.GAP_THRESHOLD).all()
