@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched gesv path on one MI355X.
+
+One step = one call of the solver over the whole batch: load, pivot search,
+row exchange, elimination with the forward substitution folded in, back
+substitution and store, all in one kernel launch.  The default workload is
+n = 32, nrhs = 1, batch = 262144, float64, column-major, A and B iid N(0, 1)
+(the recipe ``n32_f64_col``; with seed 0 no system needs a pivot-gap redraw,
+which the test suite checks), inputs resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is systems solved per second; the roofline
+object prices the kernel's algorithmic HBM bytes per launch against 8 TB/s;
+``cpu_baseline`` is the plain CPU oracle timed on this host's cores on the
+same inputs.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+  python bench.py --calibrate-copy      # a plain 1 GiB device copy, for
+                                        # scaling the HBM byte counters
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+FP64_VECTOR_PEAK_TFLOPS = 78.6   # MI355X, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+METRIC = "systems/sec + achieved HBM GB/s, batched LUPP gesv n=32 fp32/fp64"
+DEFAULT_WORKLOAD = "n32_f64_col"
+
+
+def algorithmic_bytes(n: int, nrhs: int, es: int) -> int:
+    """Bytes the method must move per system: A read once, B read once, X,
+    piv and info written once."""
+    return n * n * es + 2 * n * nrhs * es + 4 * n + 4
+
+
+def algorithmic_flops(n: int, nrhs: int) -> int:
+    """Per system: elimination 2*sum(m^2) multiply-add flops plus sum(m)
+    divisions (m = n-1 .. 1), forward and back substitution on nrhs columns
+    2*n*(n-1) + n each."""
+    s2 = sum(m * m for m in range(1, n))
+    s1 = sum(range(1, n))
+    return 2 * s2 + s1 + nrhs * (2 * n * (n - 1) + n)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_linear_solvers_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, launches_per_profile: int = 1):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"gesv_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    src.uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "reps": reps, "ms": dt * 1e3, "gbs": 2 * nbytes / dt / 1e9}), flush=True)
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
+    """The CPU oracle, as it stands, on all cores of this host, over the
+    same inputs; repeated until at least ``min_seconds`` of work."""
+    sys.path.insert(0, ROOT)
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    A = np.ascontiguousarray(w.A)
+    B = np.ascontiguousarray(w.B)
+    # size one pass: the whole batch, or a prefix when a pass is too long
+    t = time.perf_counter()
+    oracle.gesv(A[:2048], B[:2048], w.n, w.nrhs, w.layout, nthreads=cores)
+    per_sys = max((time.perf_counter() - t) / 2048, 1e-9)
+    count = int(min(w.batch, max(2048, max_seconds / 3 / per_sys)))
+    As, Bs = A[:count], B[:count]
+    passes, solved = 0, 0
+    t = time.perf_counter()
+    while True:
+        oracle.gesv(As, Bs, w.n, w.nrhs, w.layout, nthreads=cores)
+        passes += 1
+        solved += count
+        el = time.perf_counter() - t
+        if el >= min_seconds or el + el / passes > max_seconds:
+            break
+    return {"value": solved / el, "unit": "systems/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {count} of the {w.batch} systems, {passes} passes, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--batch", type=int, default=0, help="override the recipe's batch")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the batched solver shards systems across GPUs "
+              "with no communication, and this build measures the one-GPU share.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    sys.path.insert(0, ROOT)
+    import dense_linear_solvers_amd as tdls
+    from dense_linear_solvers_amd import workloads
+
+    t_gen = time.perf_counter()
+    w = workloads.make(args.workload, seed=0, batch=args.batch or None)
+    print(f"[bench] inputs {w.name} n={w.n} nrhs={w.nrhs} batch={w.batch} {w.dtype} "
+          f"{w.layout} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(w.A).to(dev)
+    B = torch.from_numpy(w.B).to(dev)
+    X = torch.empty_like(B)
+    piv = torch.empty((w.batch, w.n), dtype=torch.int32, device=dev)
+    info = torch.empty((w.batch,), dtype=torch.int32, device=dev)
+    out = (X, piv, info)
+    stream = torch.cuda.current_stream(dev)
+    plan = tdls.plan_gesv(w.dtype, w.layout, w.n, w.nrhs, w.batch)
+
+    for _ in range(args.warmup):
+        tdls.gesv_batched(A, B, w.layout, out=out)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        tdls.gesv_batched(A, B, w.layout, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    # sanity of the timed output (no oracle here): status and a residual sample
+    info_h = info.cpu().numpy()
+    rng = np.random.default_rng(0)
+    sample = torch.from_numpy(rng.choice(w.batch, size=min(w.batch, 512), replace=False)).to(dev)
+    As = A[sample].double()
+    Xs = X[sample].double()
+    Bs = B[sample].double()
+    if w.layout == "col":
+        As, Xs, Bs = As.transpose(1, 2), Xs.transpose(1, 2), Bs.transpose(1, 2)
+    res = (torch.bmm(As.contiguous(), Xs.contiguous()) - Bs).abs().amax(dim=(1, 2))
+    eps = 2.0 ** -52 if w.dtype == "f64" else 2.0 ** -23
+    den = w.n * eps * As.abs().sum(dim=2).amax(dim=1) * Xs.abs().amax(dim=(1, 2))
+    ok = info[sample] == 0
+    resid_max = float((res[ok] / den[ok]).max().item()) if bool(ok.any()) else 0.0
+
+    es = 8 if w.dtype == "f64" else 4
+    bytes_per_launch = algorithmic_bytes(w.n, w.nrhs, es) * w.batch
+    flops_per_launch = algorithmic_flops(w.n, w.nrhs) * w.batch
+    achieved_gbs = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
+    achieved_tflops = flops_per_launch / (kernel_ms * 1e-3) / 1e12
+    vec_peak = FP64_VECTOR_PEAK_TFLOPS if w.dtype == "f64" else FP32_VECTOR_PEAK_TFLOPS
+    systems_per_s = w.batch / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": systems_per_s,
+        "unit": "systems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
+                   "layout": "column-major" if w.layout == "col" else "row-major",
+                   "distribution": w.meta.get("recipe"), "seed": 0,
+                   "group_size": plan["group_size"], "systems_per_wave": plan["systems_per_wave"]},
+        "kernel_ms": kernel_ms,
+        "hbm_gbs_algorithmic": achieved_gbs,
+        "vector_tflops_algorithmic": achieved_tflops,
+        "vector_frac": achieved_tflops / vec_peak,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name)},
+        "check": {"failed_systems": int((info_h != 0).sum()), "residual_max_sample": resid_max},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+"""ctypes binding of libtdls.so: argument marshalling only.
+
+Every computation happens in the library's HIP kernels; this module turns
+torch tensors into the raw pointers, sizes and stream of the C interface and
+allocates the outputs.  There is no fallback: without the built library, or
+without a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+F32, F64 = 0, 1
+ROW_MAJOR, COL_MAJOR = 0, 1
+_LAYOUTS = {"row": ROW_MAJOR, "col": COL_MAJOR}
+
+_lib = None
+
+
+class TdlsError(RuntimeError):
+    """A non-zero return code of the C interface."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("nrhs", ctypes.c_int), ("n_kernel", ctypes.c_int),
+                ("nrhs_kernel", ctypes.c_int), ("group_size", ctypes.c_int),
+                ("rows_per_lane", ctypes.c_int), ("systems_per_wave", ctypes.c_int),
+                ("threads_per_block", ctypes.c_int), ("systems_per_block", ctypes.c_int64),
+                ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+EXPORTED = ("tdls_gesv_batched", "tdls_plan_gesv", "tdls_strerror", "tdls_version")
+
+
+def library_path() -> str:
+    return _build.library_path()
+
+
+def load_library():
+    """Load libtdls.so (building it first only when no build exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    lib.tdls_gesv_batched.restype = ctypes.c_int
+    lib.tdls_gesv_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.tdls_plan_gesv.restype = ctypes.c_int
+    lib.tdls_plan_gesv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int64, ctypes.POINTER(Plan)]
+    lib.tdls_strerror.restype = ctypes.c_char_p
+    lib.tdls_strerror.argtypes = [ctypes.c_int]
+    lib.tdls_version.restype = ctypes.c_char_p
+    lib.tdls_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().tdls_strerror(int(code)).decode()
+
+
+def version() -> str:
+    return load_library().tdls_version().decode()
+
+
+def tdls_gesv_batched(dtype: int, layout: int, n: int, nrhs: int, batch: int, A: int, B: int,
+                      X: int, piv: int, info: int, stream: int) -> int:
+    """The C call itself, raw pointers (ints) in, return code out."""
+    return int(load_library().tdls_gesv_batched(int(dtype), int(layout), int(n), int(nrhs),
+                                                int(batch), A, B, X, piv, info, stream))
+
+
+def tdls_plan_gesv(dtype: int, layout: int, n: int, nrhs: int, batch: int):
+    """The planner call: returns (code, Plan)."""
+    p = Plan()
+    rc = int(load_library().tdls_plan_gesv(int(dtype), int(layout), int(n), int(nrhs),
+                                           int(batch), ctypes.byref(p)))
+    return rc, p
+
+
+def plan_gesv(dtype: str, layout: str, n: int, nrhs: int, batch: int) -> dict:
+    rc, p = tdls_plan_gesv(F64 if dtype == "f64" else F32, _LAYOUTS[layout], n, nrhs, batch)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_plan_gesv")
+    return p.as_dict()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def gesv_batched(A, B, layout: str = "row", out=None, stream=None):
+    """Solve a batch of systems held in torch CUDA tensors.
+
+    A: [batch, n, n] storage of the matrices in ``layout`` (for "col" each
+    A[s] holds the transpose of the logical matrix).  B: [batch, n, nrhs]
+    ("row") or [batch, nrhs, n] ("col").  float32 or float64, contiguous,
+    same device.  Returns (X, piv, info) with X shaped like B, piv int32
+    [batch, n], info int32 [batch].  ``out`` may pass preallocated (X, piv,
+    info).  Runs on ``stream`` (default: the current stream) and does not
+    synchronize.
+    """
+    torch = _torch()
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'row' or 'col'")
+    if A.dtype not in (torch.float32, torch.float64) or B.dtype != A.dtype:
+        raise TypeError("A and B must both be float32 or both float64")
+    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
+        raise ValueError("A and B must be CUDA tensors on the same device")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous")
+    if A.dim() != 3 or A.shape[1] != A.shape[2]:
+        raise ValueError("A must be [batch, n, n]")
+    batch, n = A.shape[0], A.shape[1]
+    if B.dim() != 3 or B.shape[0] != batch:
+        raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
+    nrhs = B.shape[2] if layout == "row" else B.shape[1]
+    if (B.shape[1] if layout == "row" else B.shape[2]) != n:
+        raise ValueError("B does not match n")
+    if out is None:
+        X = torch.empty_like(B)
+        piv = torch.empty((batch, n), dtype=torch.int32, device=A.device)
+        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+    else:
+        X, piv, info = out
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        rc = tdls_gesv_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
+                               nrhs, batch, A.data_ptr(), B.data_ptr(), X.data_ptr(),
+                               piv.data_ptr(), info.data_ptr(), s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_gesv_batched")
+    return X, piv, info

@@ -1,0 +1,44 @@
+// One shape's launcher: compiled once per entry of TDLS_FOR_EACH_SHAPE with
+// -DTDLS_INST_SFX=<f32|f64> -DTDLS_INST_REAL=<float|double>
+// -DTDLS_INST_N=<N> -DTDLS_INST_NRHS=<NRHS>, so that the kernels build in
+// parallel.
+#include "gesv_kernel.hpp"
+
+#if !defined(TDLS_INST_SFX) || !defined(TDLS_INST_REAL) || !defined(TDLS_INST_N) || \
+    !defined(TDLS_INST_NRHS)
+#error "gesv_inst.hip is compiled once per shape with the TDLS_INST_* macros defined"
+#endif
+
+#define TDLS_LAUNCHER_NAME_(sfx, N, NRHS) launch_gesv_##sfx##_n##N##_r##NRHS
+#define TDLS_LAUNCHER_NAME(sfx, N, NRHS) TDLS_LAUNCHER_NAME_(sfx, N, NRHS)
+
+namespace tdls {
+
+template <typename Real, int N, int NRHS, int T>
+static int launch_instance(const LaunchPlan& p, const void* A, const void* B, void* X,
+                           int32_t* piv, int32_t* info, hipStream_t stream) {
+  hipLaunchKernelGGL((gesv_kernel<Real, N, NRHS, T>), dim3((unsigned)p.grid),
+                     dim3(p.threads_per_block), 0, stream, p.layout, p.n, p.nrhs, p.batch,
+                     static_cast<const Real*>(A), static_cast<const Real*>(B),
+                     static_cast<Real*>(X), piv, info);
+  return (int)hipGetLastError();
+}
+
+int TDLS_LAUNCHER_NAME(TDLS_INST_SFX, TDLS_INST_N, TDLS_INST_NRHS)(
+    const LaunchPlan& p, const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
+    hipStream_t stream) {
+  using Real = TDLS_INST_REAL;
+  constexpr int N = TDLS_INST_N;
+  constexpr int NRHS = TDLS_INST_NRHS;
+  constexpr bool is64 = sizeof(Real) == 8;
+  constexpr int T0 = pick_group_size(N, NRHS, is64);
+  constexpr int T1 = alt_group_size(N, NRHS, is64);
+  if (p.N != N || p.NRHS != NRHS) return (int)hipErrorInvalidConfiguration;
+  if (p.T == T0) return launch_instance<Real, N, NRHS, T0>(p, A, B, X, piv, info, stream);
+  if constexpr (T1 != 0) {
+    if (p.T == T1) return launch_instance<Real, N, NRHS, T1>(p, A, B, X, piv, info, stream);
+  }
+  return (int)hipErrorInvalidConfiguration;
+}
+
+}  // namespace tdls

@@ -1,0 +1,96 @@
+// Internal declarations shared by the host-side entry points and the kernel
+// translation units.  Not part of the public interface (include/tdls.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdls {
+
+// Compile-time shapes the kernels are built for, as X(sfx, Real, N, NRHS).
+// A call with n <= N and nrhs <= NRHS runs the smallest such (N, NRHS)
+// kernel with the matrix padded by an identity block and the right-hand
+// sides by zero columns (see the loader).  The build script reads this list.
+#define TDLS_FOR_EACH_SHAPE(X)                                                              \
+  X(f32, float, 8, 1) X(f32, float, 8, 2) X(f32, float, 8, 4) X(f32, float, 8, 8)            \
+  X(f32, float, 16, 1) X(f32, float, 16, 2) X(f32, float, 16, 4) X(f32, float, 16, 8)        \
+  X(f32, float, 24, 1) X(f32, float, 24, 2) X(f32, float, 24, 4) X(f32, float, 24, 8)        \
+  X(f32, float, 32, 1) X(f32, float, 32, 2) X(f32, float, 32, 4) X(f32, float, 32, 8)        \
+  X(f32, float, 48, 1) X(f32, float, 48, 2) X(f32, float, 48, 4) X(f32, float, 48, 8)        \
+  X(f32, float, 64, 1) X(f32, float, 64, 2) X(f32, float, 64, 4) X(f32, float, 64, 8)        \
+  X(f64, double, 8, 1) X(f64, double, 8, 2) X(f64, double, 8, 4) X(f64, double, 8, 8)        \
+  X(f64, double, 16, 1) X(f64, double, 16, 2) X(f64, double, 16, 4) X(f64, double, 16, 8)    \
+  X(f64, double, 24, 1) X(f64, double, 24, 2) X(f64, double, 24, 4) X(f64, double, 24, 8)    \
+  X(f64, double, 32, 1) X(f64, double, 32, 2) X(f64, double, 32, 4) X(f64, double, 32, 8)    \
+  X(f64, double, 48, 1) X(f64, double, 48, 2) X(f64, double, 48, 4) X(f64, double, 48, 8)    \
+  X(f64, double, 64, 1) X(f64, double, 64, 2) X(f64, double, 64, 4) X(f64, double, 64, 8)
+
+constexpr int kNumN = 6;
+constexpr int kNValues[kNumN] = {8, 16, 24, 32, 48, 64};
+constexpr int kNumNrhs = 4;
+constexpr int kNrhsValues[kNumNrhs] = {1, 2, 4, 8};
+
+constexpr int kWaveSize = 64;
+constexpr int kWavesPerBlock = 4;
+
+// Everything a launch needs, decided on the host before any launch.
+struct LaunchPlan {
+  int dtype;          // 0 f32, 1 f64
+  int layout;         // 0 row-major, 1 column-major
+  int n, nrhs;        // problem
+  int N, NRHS;        // kernel instantiation (N >= n, NRHS >= nrhs)
+  int T;              // lanes per system (group size), power of two
+  int R;              // rows per lane, ceil(N / T)
+  int G;              // systems per wave, 64 / T
+  int64_t batch;
+  int64_t systems_per_block;
+  int64_t grid;
+  int threads_per_block;
+  int lds_bytes;
+};
+
+// Group size chosen at compile time for each instantiation.  Registers per
+// lane for the data rows are R * (N + NRHS) * (element size / 4); the rule
+// keeps that under a budget, taking the largest R (fewest lanes per system,
+// so that the per-step cross-lane work is shared by the most systems).
+constexpr int pick_group_size(int N, int NRHS, bool is64) {
+  const int words = is64 ? 2 : 1;
+  const int budget = 136;
+  int best = 64;
+  for (int T = 64; T >= 1; T /= 2) {
+    const int R = (N + T - 1) / T;
+    if (R * (N + NRHS) * words <= budget) best = T;
+  }
+  return best;
+}
+
+// A second group size built for the smaller shapes: one row per lane (the
+// smallest power of two >= N), when that differs from the default.  Results
+// do not depend on the group size (the arithmetic and its order are the
+// same), which the tests check bit for bit.  0 when none is built.
+constexpr int alt_group_size(int N, int NRHS, bool is64) {
+  int t = 1;
+  while (t < N && t < 64) t *= 2;
+  return (N <= 32 && t != pick_group_size(N, NRHS, is64)) ? t : 0;
+}
+
+// Exchange records: per group, 2 buffers x 2 records of N + NRHS entries
+// with an odd pitch.
+constexpr int gesv_group_elems(int N, int NRHS) { return 4 * (N + NRHS + 1); }
+constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
+  return kWavesPerBlock * (kWaveSize / T) * gesv_group_elems(N, NRHS) * (is64 ? 8 : 4);
+}
+
+// Launchers, one per shape of TDLS_FOR_EACH_SHAPE, defined in the
+// instantiation translation units.  They enqueue the kernel of p.T and
+// return a hipError_t value cast to int.
+using GesvLauncher = int (*)(const LaunchPlan& p, const void* A, const void* B, void* X,
+                             int32_t* piv, int32_t* info, hipStream_t stream);
+#define TDLS_DECLARE_LAUNCHER(sfx, Real, N, NRHS)                                              \
+  int launch_gesv_##sfx##_n##N##_r##NRHS(const LaunchPlan& p, const void* A, const void* B,  \
+                                         void* X, int32_t* piv, int32_t* info,                \
+                                         hipStream_t stream);
+TDLS_FOR_EACH_SHAPE(TDLS_DECLARE_LAUNCHER)
+#undef TDLS_DECLARE_LAUNCHER
+
+}  // namespace tdls

@@ -1,0 +1,144 @@
+/*
+ * tdls.h -- C interface of the MI355X (gfx950) batched small-system solver.
+ *
+ * One call solves `batch` independent dense systems A_s X_s = B_s, each n x n
+ * with 1..8 right-hand sides, by LU factorization with partial row pivoting
+ * followed by forward and back substitution (LAPACK's gesv, one system per
+ * group of lanes of a GPU wavefront).
+ *
+ * Where the operation is defined (page title, section):
+ *   - "solver_static.hpp File Reference" (TDLS CooperativeLUpp solver),
+ *     Detailed Description: right-looking LU with partial pivoting held in
+ *     the registers of a group of threads, one system per group, with the
+ *     forward substitution folded into the factorization and the back
+ *     substitution U x = y; the layout flag of that page selects row- or
+ *     column-major storage of A.
+ *   - "ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged
+ *     numerical and failure contract, and section on support and
+ *     trade-offs: [batch, n, n] / [batch, n, nrhs] inputs, partial ROW
+ *     pivoting with the lowest row number winning ties, no reciprocal
+ *     approximation, status 0 / first failed pivot, a failed system gets
+ *     zeroed results and pivots -1, inputs read-only with separate output
+ *     buffers, host validation before any launch, no kernel for an empty
+ *     batch and exactly one kernel otherwise, errors instead of silent
+ *     fallbacks.
+ *
+ * Reading taken for the row-major layout: the rows of A are pivoted in both
+ * layouts (P A = L U); the layout flag only changes how elements are
+ * addressed.
+ */
+#ifndef TDLS_H
+#define TDLS_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of A, B and X. */
+typedef enum tdls_dtype {
+  TDLS_F32 = 0, /* IEEE binary32, every operation in binary32 */
+  TDLS_F64 = 1  /* IEEE binary64, every operation in binary64 */
+} tdls_dtype;
+
+/* Storage order of each system's A, B and X (the same flag for all three). */
+typedef enum tdls_layout {
+  TDLS_ROW_MAJOR = 0, /* A(r,c) at r*n + c;  B(r,j), X(r,j) at r*nrhs + j */
+  TDLS_COL_MAJOR = 1  /* A(r,c) at c*n + r;  B(r,j), X(r,j) at j*n + r    */
+} tdls_layout;
+
+/* Return codes of the calls (not the per-system status, see `info`). */
+#define TDLS_SUCCESS 0
+/* -1 .. -10: the i-th argument of tdls_gesv_batched is invalid (LAPACK style). */
+#define TDLS_ERR_LAUNCH (-100)      /* the HIP launch failed (see tdls_strerror) */
+#define TDLS_ERR_DEVICE (-101)      /* the current device is not gfx950 */
+#define TDLS_ERR_HIP (-102)         /* a HIP query failed */
+#define TDLS_ERR_NO_KERNEL (-103)   /* no kernel built for the planned shape */
+
+/* What tdls_gesv_batched would launch for a given problem (host only). */
+typedef struct tdls_plan {
+  int n, nrhs;               /* the problem */
+  int n_kernel;              /* compile-time size the kernel is built for (>= n) */
+  int nrhs_kernel;           /* compile-time right-hand sides (>= nrhs) */
+  int group_size;            /* T: lanes cooperating on one system */
+  int rows_per_lane;         /* R = ceil(n_kernel / T) */
+  int systems_per_wave;      /* 64 / T */
+  int threads_per_block;
+  int64_t systems_per_block;
+  int64_t grid;              /* blocks launched (0 for an empty batch) */
+  int lds_bytes;             /* LDS per block */
+} tdls_plan;
+
+/*
+ * Solve A_s X_s = B_s for s = 0 .. batch-1 on `stream`.
+ *
+ * Arguments (the number in brackets is the error code returned when the
+ * argument is rejected, as -i):
+ *   [1] dtype   TDLS_F32 or TDLS_F64.
+ *   [2] layout  TDLS_ROW_MAJOR or TDLS_COL_MAJOR; applies to A, B and X.
+ *   [3] n       1 <= n <= 64.
+ *   [4] nrhs    1 <= nrhs <= 8.
+ *   [5] batch   >= 0.  0 launches nothing and returns TDLS_SUCCESS.
+ *   [6] A       device pointer, batch * n * n elements, system s at s*n*n;
+ *               read only.  Aligned to the element size.
+ *   [7] B       device pointer, batch * n * nrhs elements, system s at
+ *               s*n*nrhs; read only.  Aligned to the element size.
+ *   [8] X       device pointer, batch * n * nrhs elements, layout of B;
+ *               written.  Must not overlap A, B, piv or info.
+ *   [9] piv     device pointer, int32 [batch][n]; written.  piv[s][k] is the
+ *               0-based row exchanged with row k at step k (LAPACK's swap
+ *               sequence), or -1 everywhere for a failed system.
+ *  [10] info    device pointer, int32 [batch]; written.  0 on success, or
+ *               k >= 1 when the pivot of step k (1-based) is exactly zero
+ *               (the first such step).  A failed system gets X = +0.0 and
+ *               piv = -1 in every entry.
+ *       stream  HIP stream (0 = the null stream).
+ *
+ * Every output entry of every system is written, so outputs need no
+ * clearing.  Ties between equal pivot magnitudes go to the lowest current
+ * row position.  Multipliers and solution entries are correctly rounded
+ * IEEE quotients.
+ *
+ * Ownership and behaviour: all buffers belong to the caller; the library
+ * allocates and frees nothing, keeps no per-call state and never
+ * synchronizes.  With batch > 0 exactly one kernel is enqueued on `stream`
+ * and the call returns at once; results are valid once the stream has
+ * reached that point.  Arguments are validated before anything is
+ * enqueued; on error nothing is launched.  Results do not depend on the
+ * group size chosen by the planner.  Non-finite inputs are accepted but
+ * their results are unspecified.
+ *
+ * Returns TDLS_SUCCESS, -i for an invalid i-th argument, or one of the
+ * TDLS_ERR_* codes.
+ */
+int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                      const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
+                      hipStream_t stream);
+
+/*
+ * Fill *out with the launch tdls_gesv_batched would make for this problem
+ * (host only: touches no device).  Validates the same scalar arguments
+ * (codes -1 .. -5); returns -6 when out is NULL.
+ *
+ * The environment variable TDLS_GROUP_SIZE, when set to a group size built
+ * for the shape, overrides the planner's choice (used by the tests that
+ * check results do not depend on it); an unbuilt value yields
+ * TDLS_ERR_NO_KERNEL from both calls.
+ */
+int tdls_plan_gesv(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                   tdls_plan* out);
+
+/* Static description of a return code (never NULL). */
+const char* tdls_strerror(int code);
+
+/* Library version string, e.g. "tdls-mi355x 0.1.0 gfx950". */
+const char* tdls_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDLS_H */

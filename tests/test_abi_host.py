@@ -1,0 +1,125 @@
+"""The C interface on the host: the library loads, exports every declared
+symbol, validates arguments and plans launches without touching a GPU.
+
+Only validation paths that return before any device call are exercised
+here: every call below either fails a scalar check, passes a null pointer,
+or names overlapping buffers, so nothing is ever launched.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_linear_solvers_amd as tdls
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tdls.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tdls.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(tdls_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_interface():
+    assert _declared_functions() == sorted(tdls.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", tdls.library_path()],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (tdls_\w+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_strerror(lib):
+    assert "gfx950" in tdls.version()
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -100, -101, -102, -103]:
+        msg = tdls.strerror(code)
+        assert msg and "unknown" not in msg, code
+    assert "unknown" in tdls.strerror(12345)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 0, 8, 1, 1), -1),
+    ((0, 5, 8, 1, 1), -2),
+    ((0, 0, 0, 1, 1), -3),
+    ((0, 0, 65, 1, 1), -3),
+    ((0, 0, 8, 0, 1), -4),
+    ((0, 0, 8, 9, 1), -4),
+    ((0, 0, 8, 1, -1), -5),
+])
+def test_scalar_validation(lib, args, code):
+    rc, _ = tdls.tdls_plan_gesv(*args)
+    assert rc == code
+    assert tdls.tdls_gesv_batched(*args, 0, 0, 0, 0, 0, 0) == code
+
+
+def test_plan_null_out(lib):
+    assert lib.tdls_plan_gesv(0, 0, 8, 1, 1, None) == -6
+
+
+def test_empty_batch_launches_nothing(lib):
+    # batch 0: success without looking at the pointers (all null here)
+    assert tdls.tdls_gesv_batched(tdls.F64, tdls.ROW_MAJOR, 32, 1, 0, 0, 0, 0, 0, 0, 0) == 0
+    p = tdls.plan_gesv("f64", "row", 32, 1, 0)
+    assert p["grid"] == 0
+
+
+def test_pointer_validation_before_launch(lib):
+    n, nrhs, batch = 16, 2, 10
+    es = 8
+    a = 1 << 40                                  # never dereferenced: every call fails
+    b = a + batch * n * n * es                   # before the device is queried
+    x = b + batch * n * nrhs * es
+    pv = x + batch * n * nrhs * es
+    inf = pv + batch * n * 4
+    call = lambda *ptrs: tdls.tdls_gesv_batched(tdls.F64, tdls.ROW_MAJOR, n, nrhs, batch,
+                                                *ptrs, 0)
+    assert call(0, b, x, pv, inf) == -6
+    assert call(a + 4, b, x, pv, inf) == -6          # misaligned for float64
+    assert call(a, 0, x, pv, inf) == -7
+    assert call(a, b, 0, pv, inf) == -8
+    assert call(a, b, a, pv, inf) == -8              # X aliases A
+    assert call(a, b, b + 8, pv, inf) == -8          # X overlaps B
+    assert call(a, b, x, 0, inf) == -9
+    assert call(a, b, x, x + 16, inf) == -9          # piv overlaps X
+    assert call(a, b, x, pv + 2, inf) == -9          # misaligned int32
+    assert call(a, b, x, pv, 0) == -10
+    assert call(a, b, x, pv, pv) == -10              # info overlaps piv
+
+
+def test_planner_shapes(lib):
+    for dtype in ("f32", "f64"):
+        for n in range(1, 65):
+            for nrhs in range(1, 9):
+                p = tdls.plan_gesv(dtype, "row", n, nrhs, 1000)
+                assert p["n_kernel"] >= n and p["nrhs_kernel"] >= nrhs
+                T = p["group_size"]
+                assert T & (T - 1) == 0 and 1 <= T <= 64
+                assert p["rows_per_lane"] * T >= p["n_kernel"]
+                assert p["systems_per_wave"] * T == 64
+                assert p["systems_per_block"] * p["grid"] >= 1000
+                assert (p["grid"] - 1) * p["systems_per_block"] < 1000
+                assert 0 < p["lds_bytes"] <= 160 * 1024
+
+
+def test_group_size_override(lib, monkeypatch):
+    base = tdls.plan_gesv("f64", "col", 32, 1, 100)
+    monkeypatch.setenv("TDLS_GROUP_SIZE", "32")
+    p = tdls.plan_gesv("f64", "col", 32, 1, 100)
+    assert p["group_size"] == 32 and base["group_size"] != 32
+    monkeypatch.setenv("TDLS_GROUP_SIZE", "3")
+    rc, _ = tdls.tdls_plan_gesv(tdls.F64, tdls.COL_MAJOR, 32, 1, 100)
+    assert rc == -103
