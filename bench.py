@@ -16,6 +16,7 @@ same inputs.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --calibrate-copy      # a plain 1 GiB device copy, for
                                         # scaling the HBM byte counters
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 """
 from __future__ import annotations
 
@@ -74,6 +75,46 @@ def measured_traffic(workload: str, launches_per_profile: int = 1):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_values(csv_dir: str, counter: str, kernel_prefix: str) -> list:
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
+        with open(f, encoding="utf-8") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(kernel_prefix):
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} values for {kernel_prefix} under {csv_dir}")
+    return vals
+
+
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                       copy_write_dir: str, copy_bytes: int = 1 << 30) -> dict:
+    """HBM bytes per launch of the solver kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for a plain device copy of ``copy_bytes`` bytes."""
+    fk = float(np.median(_counter_values(fetch_dir, "FETCH_SIZE", "gesv")))
+    wk = float(np.median(_counter_values(write_dir, "WRITE_SIZE", "gesv")))
+    cf = float(np.median(_counter_values(copy_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")))
+    cw = float(np.median(_counter_values(copy_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")))
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    fetch_b = fk * 1024.0 * fetch_scale
+    write_b = wk * 1024.0 * write_scale
+    d = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+         "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+         "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+         "fetch_scale": fetch_scale, "write_scale": write_scale,
+         "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+         "hbm_bytes_per_launch": fetch_b + write_b}
+    out = os.path.join(ROOT, "profiles", f"gesv_{workload}_traffic.json")
+    with open(out, "w", encoding="utf-8") as fh:
+        json.dump(d, fh, indent=1)
+        fh.write("\n")
+    return d
+
+
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -125,7 +166,14 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the recipe's batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                             "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/gesv_<workload>_traffic.json from rocprofv3 --pmc "
+                         "output directories (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.workload, *args.summarize_counters), indent=1))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
