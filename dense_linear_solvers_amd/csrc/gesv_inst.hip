@@ -2,7 +2,7 @@
 // -DTDLS_INST_SFX=<f32|f64> -DTDLS_INST_REAL=<float|double>
 // -DTDLS_INST_N=<N> -DTDLS_INST_NRHS=<NRHS>, so that the kernels build in
 // parallel.
-#include "gesv_kernel.hpp"
+#include "gesv_panel.hpp"
 
 #if !defined(TDLS_INST_SFX) || !defined(TDLS_INST_REAL) || !defined(TDLS_INST_N) || \
     !defined(TDLS_INST_NRHS)
@@ -17,9 +17,14 @@ namespace tdls {
 template <typename Real, int N, int NRHS, int T>
 static int launch_instance(const LaunchPlan& p, const void* A, const void* B, void* X,
                            int32_t* piv, int32_t* info, hipStream_t stream) {
-  hipLaunchKernelGGL((gesv_kernel<Real, N, NRHS, T>), dim3((unsigned)p.grid),
-                     dim3(p.threads_per_block), 0, stream, p.layout, p.n, p.nrhs, p.batch,
-                     static_cast<const Real*>(A), static_cast<const Real*>(B),
+  constexpr int PB = panel_width(N, NRHS, sizeof(Real) == 8);
+  using S = PanelShape<Real, N, NRHS, T, PB>;
+  static_assert(S::BLOCK_BYTES == gesv_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
+                "host and device LDS sizes disagree");
+  if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB>), dim3((unsigned)p.grid),
+                     dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
+                     p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),
                      static_cast<Real*>(X), piv, info);
   return (int)hipGetLastError();
 }

@@ -1,0 +1,542 @@
+// Batched gesv, panel kernel: LU with partial row pivoting plus forward and
+// back substitution, one n x n system per group of T lanes (T = 4, 16 or 64)
+// of a wave64, rows held in VGPRs.
+//
+// What is computed (cited by page title and section):
+//  * "solver_static.hpp File Reference" (TDLS CooperativeLUpp), Detailed
+//    Description: right-looking LU with partial pivoting of rows held by a
+//    group of lanes, lane tx holding rows tx, tx+T, ...; the forward
+//    substitution L y = P b carried by every elimination step, then U x = y.
+//    Its logical row interchanges (rows never move, each row tracks its
+//    position in the pivoted order) are the scheme used here.  "Departures
+//    from the MAGMA kernel": several systems per wave, phantom rows skipped,
+//    each solution entry kept by the lane owning its row, a zero pivot
+//    replaced by a divisor of 1.  "Fixed barrier sequence": the sequence of
+//    exchanges never depends on the data.
+//  * "ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged
+//    numerical and failure contract: partial row pivoting, ties to the
+//    lowest row number, exact quotients, status 0 / first failed pivot,
+//    failed systems zeroed with pivots -1, read-only inputs.
+//
+// Arithmetic: every element receives exactly the fused multiply-adds of the
+// unblocked right-looking algorithm, in the same order (step by step), so
+// results do not depend on the blocking below.
+//
+// gfx950 design.  Moving a row out of one lane costs one LDS write
+// instruction per 16 bytes whatever the number of active lanes, while a DPP
+// broadcast from a fixed lane of a 16-lane row rides for free on the fused
+// multiply-add (v_fmac_*_dpp row_newbcast / quad_perm).  The factorization
+// therefore goes by panels of B columns:
+//   * inside a panel, step k updates only column k (with the panel's earlier
+//     pivots, their value fetched from the owning lane by ds_bpermute), finds
+//     the pivot (three DPP max/min passes on the key |a|, then lowest
+//     position), relabels, and forms the multipliers by IEEE division;
+//   * at the end of the panel, each of its B pivot rows is written once to an
+//     LDS record (trailing columns, right-hand sides, its multipliers inside
+//     the panel); every lane reads back the entries it serves as DPP source
+//     (trailing column t from lane t mod 16), the panel's own updates are
+//     applied to those copies (a small triangular solve), and every row of
+//     the group takes the panel's B rank-1 updates on its trailing columns in
+//     step order, the pivot-row entry broadcast by DPP inside the FMA.
+// Back substitution, k = n-1 .. 0: the owner of position k divides, the
+// quotient reaches the group by ds_bpermute (readlane when T = 64), and the
+// rows above k fold it in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "tdls_internal.h"
+
+namespace tdls {
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    sfor<B + 1, E>(f);
+  }
+}
+
+template <typename Real>
+struct RealTraits;
+template <>
+struct RealTraits<float> {
+  typedef float vec16 __attribute__((ext_vector_type(4)));
+  static constexpr int VEC = 4;
+};
+template <>
+struct RealTraits<double> {
+  typedef double vec16 __attribute__((ext_vector_type(2)));
+  static constexpr int VEC = 2;
+};
+
+template <typename Real, int N, int NRHS, int T, int B>
+struct PanelShape {
+  static_assert(T == 4 || T == 16 || T == 64, "group size must be 4, 16 or 64");
+  static constexpr int R = (N + T - 1) / T;        // rows (slots) per lane
+  static constexpr int G = kWaveSize / T;          // systems per wave
+  static constexpr int SL = T < 16 ? T : 16;       // lanes per DPP broadcast domain
+  static constexpr int VEC = RealTraits<Real>::VEC;
+  static constexpr int REC = N + NRHS;             // largest record: panel 0
+  static constexpr int REC_STRIDE = (REC + VEC - 1) / VEC * VEC;
+  static constexpr int GROUP_ELEMS = B * REC_STRIDE;
+  static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
+  static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
+  static constexpr int OWN_WORDS = (N + 3) / 4;    // 8-bit owner code per position
+  static_assert(T * R <= 256, "owner code (slot * T + lane) must fit in 8 bits");
+};
+
+// ---------------------------------------------------------------- lanes
+
+// Reduction over the T lanes of a group (groups are aligned, T | 64).
+template <int T, bool MAX>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  if constexpr (T == 4 || T == 16 || T == 64) {
+    if constexpr (T == 4) {
+      v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true));  // xor 1
+      v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, true));  // xor 2
+    } else {
+      v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, true));  // ror 8
+      v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, true));  // ror 4
+      v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, true));  // ror 2
+      v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, true));  // ror 1
+      if constexpr (T == 64) {
+        // every 16-lane row holds its own result: combine the four rows
+        uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+        uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+        uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+        uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+        v = op(op(r0, r1), op(r2, r3));
+      }
+    }
+  }
+  return v;
+}
+
+// Value of `x` held by lane `src` (absolute lane index) of this wave.
+template <int T>
+__device__ __forceinline__ double lane_fetch(double x, int src) {
+  if constexpr (T == 64) {
+    const int s = __builtin_amdgcn_readfirstlane(src);
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, s);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), s);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  } else {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  }
+}
+template <int T>
+__device__ __forceinline__ float lane_fetch(float x, int src) {
+  if constexpr (T == 64) {
+    const int s = __builtin_amdgcn_readfirstlane(src);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), s));
+  } else {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+  }
+}
+
+// acc += (u taken from lane L of its DPP domain) * m, one fused multiply-add.
+// The DPP source must not have been written by a VALU instruction in the two
+// preceding cycles; the s_nop provides them whatever the schedule.
+template <int T, int L>
+__device__ __forceinline__ void fmac_bcast(double& acc, double u, double m) {
+  if constexpr (T >= 16) {
+    asm volatile("s_nop 1\n\tv_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(u), "v"(m), "i"(L));
+  } else {
+    // 64-bit DPP allows only row_newbcast: move the two halves across the quad
+    const uint64_t b = __builtin_bit_cast(uint64_t, u);
+    constexpr int qp = L | (L << 2) | (L << 4) | (L << 6);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, qp, 0xf, 0xf, true);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), qp, 0xf, 0xf, true);
+    acc = __builtin_fma(__builtin_bit_cast(double, ((uint64_t)hi << 32) | lo), m, acc);
+  }
+}
+template <int T, int L>
+__device__ __forceinline__ void fmac_bcast(float& acc, float u, float m) {
+  if constexpr (T >= 16) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(u), "v"(m), "i"(L));
+  } else {
+    constexpr int qp = L | (L << 2) | (L << 4) | (L << 6);
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[%3,%3,%3,%3] row_mask:0xf "
+                 "bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(u), "v"(m), "i"(L));
+    (void)qp;
+  }
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ uint32_t hi_word(double v) {
+  return (uint32_t)(__builtin_bit_cast(uint64_t, v) >> 32);
+}
+__device__ __forceinline__ uint32_t lo_word(double v) {
+  return (uint32_t)__builtin_bit_cast(uint64_t, v);
+}
+
+// ------------------------------------------------------------- kernel
+
+template <typename Real, int N, int NRHS, int T, int B>
+__global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
+    gesv_panel_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ A,
+                      const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ piv,
+                      int32_t* __restrict__ info) {
+  using S = PanelShape<Real, N, NRHS, T, B>;
+  constexpr int R = S::R;
+  constexpr int G = S::G;
+  constexpr int SL = S::SL;
+  constexpr int VEC = S::VEC;
+  constexpr bool is64 = sizeof(Real) == 8;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x / kWaveSize;
+  const int g = lane / T;
+  const int tx = lane & (T - 1);
+  const int gbase = g * T;  // first lane of the group
+  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * G;
+  if (wave_first >= batch) return;  // the whole wave is past the batch
+  const int64_t sys = wave_first + g;
+  const bool live = sys < batch;
+
+  unsigned char* wave_lds = lds_raw + wave * S::WAVE_BYTES;
+  Real* rec = reinterpret_cast<Real*>(wave_lds) + g * S::GROUP_ELEMS;
+
+  Real a[R][N];
+  Real y[R][NRHS];
+  int lab[R];   // current position of the row in slot K (LAPACK order), -1 for phantom
+  int pv[R];    // pivot output for the fixed position tx + K*T
+  uint32_t own[S::OWN_WORDS];
+
+  // ---- load: slot K of lane tx holds original row q = tx + K*T.  Rows and
+  // columns n..N-1 form an identity block, right-hand sides nrhs..NRHS-1 are
+  // zero.  Phantom rows (q >= N) and the groups past the batch load row 0 of
+  // a valid system: they never take part (never a candidate, never a pivot,
+  // never stored), so their contents do not matter.  When the problem has the
+  // kernel's shape every address is a per-slot base plus a compile-time
+  // offset and every load lands directly in its row register.
+  {
+    const Real* As = A + (live ? sys : 0) * (int64_t)n * n;
+    const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
+    if (n == N && nrhs == NRHS) {
+      auto load_exact = [&](auto colc) {
+        constexpr bool COL = decltype(colc)::value;
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const int q = tx + K * T;
+          const int qq = q < N ? q : 0;
+          const Real* ar = As + (COL ? qq : qq * N);
+          const Real* br = Bs + (COL ? qq : qq * NRHS);
+          sfor<0, N>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            a[K][c] = ar[COL ? c * N : c];
+          });
+          sfor<0, NRHS>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            y[K][j] = br[COL ? j * N : j];
+          });
+        });
+      };
+      if (col)
+        load_exact(std::true_type{});
+      else
+        load_exact(std::false_type{});
+    } else {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        const bool qrow = live && q < n;
+        const int qq = qrow ? q : 0;
+        const int64_t cs = col ? n : 1;          // element stride between columns
+        const Real* ar = As + (col ? qq : (int64_t)qq * n);
+        const int64_t js = col ? n : 1;
+        const Real* br = Bs + (col ? qq : (int64_t)qq * nrhs);
+        // identity block, then the stored entries; the scheduling barriers
+        // keep few loads (and their 64-bit addresses) in flight at a time
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          a[K][c] = (q == c) ? Real(1) : Real(0);
+        });
+        sfor<0, NRHS>([&](auto jc) { y[K][decltype(jc)::value] = Real(0); });
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if (qrow && c < n) a[K][c] = ar[c * cs];
+          if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+        });
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if (qrow && j < nrhs) y[K][j] = br[j * js];
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      lab[K] = q < N ? q : -1;
+      pv[K] = q;
+    });
+    sfor<0, S::OWN_WORDS>([&](auto wc) { own[decltype(wc)::value] = 0u; });
+  }
+
+  int status = 0;
+
+  // ---- factorization, panel by panel
+  constexpr int NP = (N + B - 1) / B;
+  sfor<0, NP>([&](auto pc) {
+    constexpr int k0 = decltype(pc)::value * B;
+    constexpr int bw = (N - k0) < B ? (N - k0) : B;   // panel width
+    constexpr int NT = N - k0 - bw;                    // trailing matrix columns
+    constexpr int W = NT + NRHS;                       // trailing entries per row
+    Real negl[B][R];                                   // -(multiplier), 0 if not below
+    int ownl[B];                                       // owning lane (absolute) of pivot i
+    int owns[B];                                       // and its slot
+
+    sfor<0, bw>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int k = k0 + i;
+      constexpr int kl = k % T;
+      constexpr int ks = k / T;
+
+      // (a) column k takes the updates of this panel's earlier pivots, in order
+      sfor<0, i>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        Real sel = a[0][k];
+        sfor<1, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          sel = owns[m] == K ? a[K][k] : sel;
+        });
+        const Real um = lane_fetch<T>(sel, ownl[m]);
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          a[K][k] = __builtin_fma(negl[m][K], um, a[K][k]);
+        });
+      });
+
+      // (b) pivot search on column k over the rows at positions >= k:
+      // largest magnitude (two passes on its bit pattern), then the lowest
+      // position among equal magnitudes.
+      uint32_t khi[R];
+      uint32_t klo[R];
+      uint32_t mhi = 0;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const bool act = lab[K] >= k;
+        uint32_t h;
+        if constexpr (is64) {
+          h = hi_word(a[K][k]);
+          klo[K] = lo_word(a[K][k]);
+        } else {
+          h = __builtin_bit_cast(uint32_t, a[K][k]);
+          klo[K] = 0;
+        }
+        khi[K] = act ? (h | 0x80000000u) : 0u;  // top bit: candidate; rest: |a| bits
+        mhi = khi[K] > mhi ? khi[K] : mhi;
+      });
+      mhi = group_reduce<T, true>(mhi);
+      uint32_t mlo = 0;
+      if constexpr (is64) {
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const uint32_t l2 = khi[K] == mhi ? klo[K] : 0u;
+          mlo = l2 > mlo ? l2 : mlo;
+        });
+        mlo = group_reduce<T, true>(mlo);
+      }
+      uint32_t kmin = 0xffffffffu;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        uint32_t sgn;
+        if constexpr (is64)
+          sgn = hi_word(a[K][k]) >> 31;
+        else
+          sgn = __builtin_bit_cast(uint32_t, a[K][k]) >> 31;
+        const uint32_t key = ((uint32_t)lab[K] << 13) | ((uint32_t)lane << 5) | (K << 1) | sgn;
+        const bool win = khi[K] == mhi && klo[K] == mlo && mhi != 0u;
+        const uint32_t k3 = win ? key : 0xffffffffu;
+        kmin = k3 < kmin ? k3 : kmin;
+      });
+      kmin = group_reduce<T, false>(kmin);
+      const bool any = kmin != 0xffffffffu;
+      const int p = any ? (int)(kmin >> 13) : k;
+      const int ol = any ? (int)((kmin >> 5) & 63u) : gbase + kl;
+      const int os = any ? (int)((kmin >> 1) & 15u) : ks;
+      const uint32_t dh = (mhi & 0x7fffffffu) | ((kmin & 1u) << 31);
+      Real dpiv;
+      if constexpr (is64)
+        dpiv = __builtin_bit_cast(double, ((uint64_t)dh << 32) | mlo);
+      else
+        dpiv = __builtin_bit_cast(float, dh);
+      const bool zero_pivot = !any || ((mhi & 0x7fffffffu) == 0u && mlo == 0u);
+      if (zero_pivot && status == 0) status = k + 1;
+      const Real d = zero_pivot ? Real(1) : dpiv;
+
+      // (c) logical interchange of positions k and p
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int old = lab[K];
+        lab[K] = old == k ? p : (old == p ? k : old);
+      });
+      ownl[i] = ol;
+      owns[i] = os;
+      own[k / 4] |= (uint32_t)((ol - gbase) + os * T) << (8 * (k % 4));
+      if (tx == kl) pv[ks] = p;
+
+      // (d) multipliers of the rows now below position k (IEEE division)
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const bool below = lab[K] > k;
+        const Real l = a[K][k] / d;
+        if (below) a[K][k] = l;
+        negl[i][K] = below ? -l : Real(0);
+      });
+    });
+
+    // ---- end of panel: pivot rows to LDS records, read back as DPP sources
+    if constexpr (W > 0) {
+      constexpr int RECN = W + bw;                           // trailing entries + multipliers
+      constexpr int NU = (W + SL - 1) / SL;                  // DPP source registers per pivot
+      auto entry = [&](auto Kc, auto ec) -> Real {
+        constexpr int K = decltype(Kc)::value;
+        constexpr int e = decltype(ec)::value;
+        if constexpr (e < NT) return a[K][k0 + bw + e];
+        else if constexpr (e < W) return y[K][e - NT];
+        else if constexpr (e < RECN) return a[K][k0 + e - W];
+        else return Real(0);
+      };
+      // The owner of each pivot row writes its record (exec-masked: an LDS
+      // write costs the same whatever the number of active lanes), one
+      // register (pair) per entry at a compile-time offset.
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int j = lab[K] - k0;
+        if (j >= 0 && j < bw) {
+          Real* dst = rec + j * S::REC_STRIDE;
+          sfor<0, RECN>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            dst[e] = entry(Kc, ec);
+          });
+        }
+      });
+      wave_sync_lds();
+
+      Real u[B][NU];
+      const int st = tx % SL;
+      sfor<0, bw>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        sfor<0, NU>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          u[m][r] = rec[m * S::REC_STRIDE + r * SL + st];   // entries past W are unused
+        });
+      });
+      // the panel's own updates of its pivot rows (entries in step order)
+      sfor<1, bw>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        sfor<0, j>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          const Real lm = rec[j * S::REC_STRIDE + W + m];
+          sfor<0, NU>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            u[j][r] = __builtin_fma(-lm, u[m][r], u[j][r]);
+          });
+        });
+      });
+      // trailing update: every row takes the panel's rank-1 updates in order
+      sfor<0, W>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        constexpr int L = e % SL;
+        constexpr int r = e / SL;
+        sfor<0, bw>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          sfor<0, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            if constexpr (e < NT)
+              fmac_bcast<T, L>(a[K][k0 + bw + e], u[m][r], negl[m][K]);
+            else
+              fmac_bcast<T, L>(y[K][e - NT], u[m][r], negl[m][K]);
+          });
+        });
+      });
+      wave_sync_lds();  // records are rewritten by the next panel
+    }
+  });
+
+  // ---- back substitution: x_k = y_k / u_kk on the owner of position k,
+  // fetched by the group, folded into the rows above k.  Each step is fenced
+  // off from the next in the schedule: the compiler would otherwise form the
+  // masked U entries of every step at once and run out of registers.
+  __builtin_amdgcn_sched_barrier(0);
+  sfor<0, N>([&](auto ic) {
+    constexpr int k = N - 1 - decltype(ic)::value;
+    const uint32_t code = (own[k / 4] >> (8 * (k % 4))) & 0xffu;
+    const int ol = gbase + (int)(code % T);
+    const int os = (int)(code / T);
+    Real dk = a[0][k];
+    sfor<1, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      dk = os == K ? a[K][k] : dk;
+    });
+    sfor<0, NRHS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      Real yk = y[0][j];
+      sfor<1, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        yk = os == K ? y[K][j] : yk;
+      });
+      const Real xk = lane_fetch<T>(yk / dk, ol);
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const Real upd = __builtin_fma(-a[K][k], xk, y[K][j]);
+        y[K][j] = lab[K] < k ? upd : (lab[K] == k ? xk : y[K][j]);
+      });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  // ---- store: X in B's layout (row of label q), piv, info
+  if (live) {
+    const int64_t nb = (int64_t)n * nrhs;
+    Real* Xs = X + sys * nb;
+    int32_t* Ps = piv + sys * (int64_t)n;
+    const bool failed = status != 0;
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int r = lab[K];
+      if (r >= 0 && r < n) {
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if (j < nrhs) {
+            const Real v = failed ? Real(0) : y[K][j];
+            if (col)
+              Xs[(int64_t)j * n + r] = v;
+            else
+              Xs[(int64_t)r * nrhs + j] = v;
+          }
+        });
+      }
+      const int q = tx + K * T;
+      if (q < n) Ps[q] = failed ? -1 : pv[K];
+    });
+    if (tx == 0) info[sys] = status;
+  }
+}
+
+}  // namespace tdls

@@ -49,36 +49,45 @@ struct LaunchPlan {
   int lds_bytes;
 };
 
-// Group size chosen at compile time for each instantiation.  Registers per
-// lane for the data rows are R * (N + NRHS) * (element size / 4); the rule
-// keeps that under a budget, taking the largest R (fewest lanes per system,
-// so that the per-step cross-lane work is shared by the most systems).
+// Group size chosen at compile time for each instantiation: the smallest of
+// 4, 16, 64 lanes whose rows fit a register budget.  Registers per lane for
+// the data rows are R * (N + NRHS) * (element size / 4) with R = ceil(N / T);
+// fewer lanes per system means more systems share each wave's pivot search,
+// divisions and exchanges.  4 and 16 lanes are DPP broadcast domains (quad,
+// row); 64 lanes is the whole wave.
+constexpr int kRegBudget = 160;
+constexpr int rows_per_lane(int N, int T) { return (N + T - 1) / T; }
+constexpr int row_regs(int N, int NRHS, int T, bool is64) {
+  return rows_per_lane(N, T) * (N + NRHS) * (is64 ? 2 : 1);
+}
 constexpr int pick_group_size(int N, int NRHS, bool is64) {
-  const int words = is64 ? 2 : 1;
-  const int budget = 136;
-  int best = 64;
-  for (int T = 64; T >= 1; T /= 2) {
-    const int R = (N + T - 1) / T;
-    if (R * (N + NRHS) * words <= budget) best = T;
-  }
-  return best;
+  if (N <= 16 && row_regs(N, NRHS, 4, is64) <= kRegBudget) return 4;
+  if (row_regs(N, NRHS, 16, is64) <= kRegBudget) return 16;
+  return 64;
 }
 
-// A second group size built for the smaller shapes: one row per lane (the
-// smallest power of two >= N), when that differs from the default.  Results
-// do not depend on the group size (the arithmetic and its order are the
-// same), which the tests check bit for bit.  0 when none is built.
+// A second group size built for the smaller shapes (the next larger of 4,
+// 16, 64), so that the tests can check that results do not depend on it
+// (the arithmetic and its order are the same).  0 when none is built.
 constexpr int alt_group_size(int N, int NRHS, bool is64) {
-  int t = 1;
-  while (t < N && t < 64) t *= 2;
-  return (N <= 32 && t != pick_group_size(N, NRHS, is64)) ? t : 0;
+  const int t0 = pick_group_size(N, NRHS, is64);
+  return (N <= 32 && t0 < 64) ? (t0 == 4 ? 16 : 64) : 0;
 }
 
-// Exchange records: per group, 2 buffers x 2 records of N + NRHS entries
-// with an odd pitch.
-constexpr int gesv_group_elems(int N, int NRHS) { return 4 * (N + NRHS + 1); }
+// Panel width of the factorization (columns whose pivot rows are exchanged
+// together through LDS).
+constexpr int panel_width(int N, [[maybe_unused]] int NRHS, [[maybe_unused]] bool is64) {
+  return N < 4 ? N : 4;
+}
+
+// LDS bytes of one block: per wave, G groups x B records of N + NRHS entries
+// (rounded up to 16 bytes).
 constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
-  return kWavesPerBlock * (kWaveSize / T) * gesv_group_elems(N, NRHS) * (is64 ? 8 : 4);
+  const int es = is64 ? 8 : 4;
+  const int vec = 16 / es;
+  const int stride = (N + NRHS + vec - 1) / vec * vec;
+  const int B = panel_width(N, NRHS, is64);
+  return kWavesPerBlock * (kWaveSize / T) * B * stride * es;
 }
 
 // Launchers, one per shape of TDLS_FOR_EACH_SHAPE, defined in the

@@ -117,9 +117,10 @@ def test_planner_shapes(lib):
 
 def test_group_size_override(lib, monkeypatch):
     base = tdls.plan_gesv("f64", "col", 32, 1, 100)
-    monkeypatch.setenv("TDLS_GROUP_SIZE", "32")
+    other = 64 if base["group_size"] != 64 else 16
+    monkeypatch.setenv("TDLS_GROUP_SIZE", str(other))
     p = tdls.plan_gesv("f64", "col", 32, 1, 100)
-    assert p["group_size"] == 32 and base["group_size"] != 32
+    assert p["group_size"] == other
     monkeypatch.setenv("TDLS_GROUP_SIZE", "3")
     rc, _ = tdls.tdls_plan_gesv(tdls.F64, tdls.COL_MAJOR, 32, 1, 100)
     assert rc == -103
