@@ -22,6 +22,14 @@ static int launch_instance(const LaunchPlan& p, const void* A, const void* B, vo
   static_assert(S::BLOCK_BYTES == gesv_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
                 "host and device LDS sizes disagree");
   if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
+  if constexpr (S::BLOCK_BYTES > 65536) {
+    // Dynamic LDS above 64 KiB has to be allowed per kernel; done once (the
+    // static is initialised thread-safely) and the outcome kept.
+    static const hipError_t allowed = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gesv_panel_kernel<Real, N, NRHS, T, PB>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, S::BLOCK_BYTES);
+    if (allowed != hipSuccess) return (int)allowed;
+  }
   hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB>), dim3((unsigned)p.grid),
                      dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                      p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),

@@ -1,5 +1,5 @@
 // Batched gesv, panel kernel: LU with partial row pivoting plus forward and
-// back substitution, one n x n system per group of T lanes (T = 4, 16 or 64)
+// back substitution, one n x n system per group of T lanes (T = 4, 16, 32, 64)
 // of a wave64, rows held in VGPRs.
 //
 // What is computed (cited by page title and section):
@@ -75,18 +75,21 @@ struct RealTraits<double> {
 
 template <typename Real, int N, int NRHS, int T, int B>
 struct PanelShape {
-  static_assert(T == 4 || T == 16 || T == 64, "group size must be 4, 16 or 64");
+  static_assert(T == 4 || T == 16 || T == 32 || T == 64, "group size must be 4, 16, 32 or 64");
   static constexpr int R = (N + T - 1) / T;        // rows (slots) per lane
   static constexpr int G = kWaveSize / T;          // systems per wave
   static constexpr int SL = T < 16 ? T : 16;       // lanes per DPP broadcast domain
   static constexpr int VEC = RealTraits<Real>::VEC;
   static constexpr int REC = N + NRHS;             // largest record: panel 0
   static constexpr int REC_STRIDE = (REC + VEC - 1) / VEC * VEC;
-  static constexpr int GROUP_ELEMS = B * REC_STRIDE;
+  // Upper-triangular store for the back substitution: row q holds columns
+  // q..N-1 then the NRHS right-hand sides, rows packed one after another.
+  static constexpr int UROW0 = N + NRHS;                    // length of row 0
+  static constexpr int UTRI = N * (N + NRHS) - N * (N - 1) / 2;
+  static constexpr int UTRI_PAD = (UTRI + VEC - 1) / VEC * VEC;   // keep 16-byte alignment
+  static constexpr int GROUP_ELEMS = (B * REC_STRIDE > UTRI_PAD ? B * REC_STRIDE : UTRI_PAD);
   static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
   static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
-  static constexpr int OWN_WORDS = (N + 3) / 4;    // 8-bit owner code per position
-  static_assert(T * R <= 256, "owner code (slot * T + lane) must fit in 8 bits");
 };
 
 // ---------------------------------------------------------------- lanes
@@ -95,7 +98,7 @@ struct PanelShape {
 template <int T, bool MAX>
 __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
   auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  if constexpr (T == 4 || T == 16 || T == 64) {
+  {
     if constexpr (T == 4) {
       v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true));  // xor 1
       v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, true));  // xor 2
@@ -104,6 +107,12 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
       v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, true));  // ror 4
       v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, true));  // ror 2
       v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, true));  // ror 1
+      if constexpr (T == 32) {
+        // combine the two 16-lane rows of each group: after the swap the
+        // first value holds row 2i in both rows of the pair, the second row 2i+1
+        const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = op((uint32_t)sw[0], (uint32_t)sw[1]);
+      }
       if constexpr (T == 64) {
         // every 16-lane row holds its own result: combine the four rows
         uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
@@ -115,6 +124,32 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
     }
   }
   return v;
+}
+
+// True, uniformly over the wave, when some group has more than one lane with
+// `pred` set.
+template <int T>
+__device__ __forceinline__ bool group_tie(bool pred) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+  if constexpr (T == 64) {
+    return __builtin_popcountll(m) > 1;
+  } else if constexpr (T == 32) {
+    return __builtin_popcount((uint32_t)m) > 1 || __builtin_popcount((uint32_t)(m >> 32)) > 1;
+  } else if constexpr (T == 16) {
+    bool tie = false;
+    sfor<0, 4>([&](auto gc) {
+      constexpr int gi = decltype(gc)::value;
+      tie = tie || __builtin_popcount((uint32_t)(m >> (16 * gi)) & 0xffffu) > 1;
+    });
+    return tie;
+  } else {
+    // lanes 4g..4g+3: a set pair inside a quad shows in (m & m >> 1), (m & m >> 2)
+    // or (m & m >> 3) at a bit whose quad offset keeps both bits in the quad
+    const uint64_t m1 = m & (m >> 1) & 0x7777777777777777ull;
+    const uint64_t m2 = m & (m >> 2) & 0x3333333333333333ull;
+    const uint64_t m3 = m & (m >> 3) & 0x1111111111111111ull;
+    return (m1 | m2 | m3) != 0;
+  }
 }
 
 // Value of `x` held by lane `src` (absolute lane index) of this wave.
@@ -144,15 +179,23 @@ __device__ __forceinline__ float lane_fetch(float x, int src) {
   }
 }
 
-// acc += (u taken from lane L of its DPP domain) * m, one fused multiply-add.
-// The DPP source must not have been written by a VALU instruction in the two
-// preceding cycles; the s_nop provides them whatever the schedule.
-template <int T, int L>
-__device__ __forceinline__ void fmac_bcast(double& acc, double u, double m) {
+// acc -= (u taken from lane L of its DPP domain) * m, one fused multiply-add
+// (the DPP source carries the negation: -u * m + acc rounds as fma(-m, u, acc)).
+// A DPP source written by a VALU instruction needs two wait states before
+// the DPP read; NOP adds them, and the caller sets it on the first read of
+// each source register after it was computed (the asm statements are volatile,
+// so they stay in program order).
+template <int T, int L, bool NOP>
+__device__ __forceinline__ void fnmac_bcast(double& acc, double u, double m) {
   if constexpr (T >= 16) {
-    asm volatile("s_nop 1\n\tv_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(acc)
-                 : "v"(u), "v"(m), "i"(L));
+    if constexpr (NOP)
+      asm volatile("s_nop 1\n\tv_fmac_f64_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(acc)
+                   : "v"(u), "v"(m), "i"(L));
+    else
+      asm volatile("v_fmac_f64_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(acc)
+                   : "v"(u), "v"(m), "i"(L));
   } else {
     // 64-bit DPP allows only row_newbcast: move the two halves across the quad
     const uint64_t b = __builtin_bit_cast(uint64_t, u);
@@ -160,22 +203,30 @@ __device__ __forceinline__ void fmac_bcast(double& acc, double u, double m) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, qp, 0xf, 0xf, true);
     const uint32_t hi =
         (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), qp, 0xf, 0xf, true);
-    acc = __builtin_fma(__builtin_bit_cast(double, ((uint64_t)hi << 32) | lo), m, acc);
+    acc = __builtin_fma(-m, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo), acc);
   }
 }
-template <int T, int L>
-__device__ __forceinline__ void fmac_bcast(float& acc, float u, float m) {
+template <int T, int L, bool NOP>
+__device__ __forceinline__ void fnmac_bcast(float& acc, float u, float m) {
   if constexpr (T >= 16) {
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(acc)
-                 : "v"(u), "v"(m), "i"(L));
+    if constexpr (NOP)
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(acc)
+                   : "v"(u), "v"(m), "i"(L));
+    else
+      asm volatile("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(acc)
+                   : "v"(u), "v"(m), "i"(L));
   } else {
-    constexpr int qp = L | (L << 2) | (L << 4) | (L << 6);
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[%3,%3,%3,%3] row_mask:0xf "
-                 "bank_mask:0xf"
-                 : "+v"(acc)
-                 : "v"(u), "v"(m), "i"(L));
-    (void)qp;
+    if constexpr (NOP)
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, -%1, %2 quad_perm:[%3,%3,%3,%3] row_mask:0xf "
+                   "bank_mask:0xf"
+                   : "+v"(acc)
+                   : "v"(u), "v"(m), "i"(L));
+    else
+      asm volatile("v_fmac_f32_dpp %0, -%1, %2 quad_perm:[%3,%3,%3,%3] row_mask:0xf bank_mask:0xf"
+                   : "+v"(acc)
+                   : "v"(u), "v"(m), "i"(L));
   }
 }
 
@@ -184,6 +235,9 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
+
+__device__ __forceinline__ float absr(float v) { return __builtin_fabsf(v); }
+__device__ __forceinline__ double absr(double v) { return __builtin_fabs(v); }
 
 __device__ __forceinline__ uint32_t hi_word(double v) {
   return (uint32_t)(__builtin_bit_cast(uint64_t, v) >> 32);
@@ -224,7 +278,6 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   Real y[R][NRHS];
   int lab[R];   // current position of the row in slot K (LAPACK order), -1 for phantom
   int pv[R];    // pivot output for the fixed position tx + K*T
-  uint32_t own[S::OWN_WORDS];
 
   // ---- load: slot K of lane tx holds original row q = tx + K*T.  Rows and
   // columns n..N-1 form an identity block, right-hand sides nrhs..NRHS-1 are
@@ -294,10 +347,17 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       lab[K] = q < N ? q : -1;
       pv[K] = q;
     });
-    sfor<0, S::OWN_WORDS>([&](auto wc) { own[decltype(wc)::value] = 0u; });
   }
 
   int status = 0;
+  // Per-slot key bits for the pivot search: position << 13 | lane << 5 |
+  // slot << 1 (the sign of the candidate goes in bit 0).  Positions are
+  // unique, so comparing keys compares positions.
+  uint32_t kb[R];
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    kb[K] = ((uint32_t)(lab[K] < 0 ? 0 : lab[K]) << 13) | ((uint32_t)lane << 5) | (K << 1);
+  });
 
   // ---- factorization, panel by panel
   constexpr int NP = (N + B - 1) / B;
@@ -306,7 +366,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     constexpr int bw = (N - k0) < B ? (N - k0) : B;   // panel width
     constexpr int NT = N - k0 - bw;                    // trailing matrix columns
     constexpr int W = NT + NRHS;                       // trailing entries per row
-    Real negl[B][R];                                   // -(multiplier), 0 if not below
+    Real lm[B][R];                                     // multiplier, 0 unless below
     int ownl[B];                                       // owning lane (absolute) of pivot i
     int owns[B];                                       // and its slot
 
@@ -327,65 +387,51 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         const Real um = lane_fetch<T>(sel, ownl[m]);
         sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          a[K][k] = __builtin_fma(negl[m][K], um, a[K][k]);
+          a[K][k] = __builtin_fma(-lm[m][K], um, a[K][k]);
         });
       });
 
-      // (b) pivot search on column k over the rows at positions >= k:
-      // largest magnitude (two passes on its bit pattern), then the lowest
-      // position among equal magnitudes.
-      uint32_t khi[R];
-      uint32_t klo[R];
-      uint32_t mhi = 0;
-      sfor<0, R>([&](auto Kc) {
+      // (b) pivot search on column k over the rows at positions >= k.  Each
+      // lane keeps its best slot (larger |a|, then lower position); the
+      // group takes the largest leading word of |a|; only when two lanes
+      // share it (rare, uniform branch) is the trailing word compared; the
+      // lowest position among the remaining ties wins.
+      Real cv = a[0][k];
+      uint32_t ck = kb[0];
+      bool cact = lab[0] >= k;
+      sfor<1, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const bool act = lab[K] >= k;
-        uint32_t h;
-        if constexpr (is64) {
-          h = hi_word(a[K][k]);
-          klo[K] = lo_word(a[K][k]);
-        } else {
-          h = __builtin_bit_cast(uint32_t, a[K][k]);
-          klo[K] = 0;
-        }
-        khi[K] = act ? (h | 0x80000000u) : 0u;  // top bit: candidate; rest: |a| bits
-        mhi = khi[K] > mhi ? khi[K] : mhi;
+        const Real v = a[K][k];
+        const bool better = absr(v) > absr(cv) || (absr(v) == absr(cv) && kb[K] < ck);
+        const bool take = act && (!cact || better);
+        cv = take ? v : cv;
+        ck = take ? kb[K] : ck;
+        cact = cact || act;
       });
-      mhi = group_reduce<T, true>(mhi);
-      uint32_t mlo = 0;
+      uint32_t chi;
+      if constexpr (is64)
+        chi = hi_word(cv);
+      else
+        chi = __builtin_bit_cast(uint32_t, cv);
+      const uint32_t sgn = chi >> 31;
+      chi = cact ? (chi | 0x80000000u) : 0u;  // top bit: candidate; rest: |a| bits
+      const uint32_t mhi = group_reduce<T, true>(chi);
+      bool top = chi == mhi && cact;
       if constexpr (is64) {
-        sfor<0, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          const uint32_t l2 = khi[K] == mhi ? klo[K] : 0u;
-          mlo = l2 > mlo ? l2 : mlo;
-        });
-        mlo = group_reduce<T, true>(mlo);
+        if (group_tie<T>(top)) {
+          const uint32_t clo = top ? lo_word(cv) : 0u;
+          const uint32_t mlo = group_reduce<T, true>(clo);
+          top = top && lo_word(cv) == mlo;
+        }
       }
-      uint32_t kmin = 0xffffffffu;
-      sfor<0, R>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        uint32_t sgn;
-        if constexpr (is64)
-          sgn = hi_word(a[K][k]) >> 31;
-        else
-          sgn = __builtin_bit_cast(uint32_t, a[K][k]) >> 31;
-        const uint32_t key = ((uint32_t)lab[K] << 13) | ((uint32_t)lane << 5) | (K << 1) | sgn;
-        const bool win = khi[K] == mhi && klo[K] == mlo && mhi != 0u;
-        const uint32_t k3 = win ? key : 0xffffffffu;
-        kmin = k3 < kmin ? k3 : kmin;
-      });
-      kmin = group_reduce<T, false>(kmin);
+      const uint32_t kmin = group_reduce<T, false>(top ? (ck | sgn) : 0xffffffffu);
       const bool any = kmin != 0xffffffffu;
       const int p = any ? (int)(kmin >> 13) : k;
       const int ol = any ? (int)((kmin >> 5) & 63u) : gbase + kl;
       const int os = any ? (int)((kmin >> 1) & 15u) : ks;
-      const uint32_t dh = (mhi & 0x7fffffffu) | ((kmin & 1u) << 31);
-      Real dpiv;
-      if constexpr (is64)
-        dpiv = __builtin_bit_cast(double, ((uint64_t)dh << 32) | mlo);
-      else
-        dpiv = __builtin_bit_cast(float, dh);
-      const bool zero_pivot = !any || ((mhi & 0x7fffffffu) == 0u && mlo == 0u);
+      const Real dpiv = lane_fetch<T>(cv, ol);  // the winner's own candidate
+      const bool zero_pivot = !any || dpiv == Real(0);
       if (zero_pivot && status == 0) status = k + 1;
       const Real d = zero_pivot ? Real(1) : dpiv;
 
@@ -393,20 +439,20 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int old = lab[K];
-        lab[K] = old == k ? p : (old == p ? k : old);
+        const int nl = old == k ? p : (old == p ? k : old);
+        lab[K] = nl;
+        kb[K] = (kb[K] & 0x1fffu) | ((uint32_t)(nl < 0 ? 0 : nl) << 13);
       });
       ownl[i] = ol;
       owns[i] = os;
-      own[k / 4] |= (uint32_t)((ol - gbase) + os * T) << (8 * (k % 4));
       if (tx == kl) pv[ks] = p;
 
-      // (d) multipliers of the rows now below position k (IEEE division)
+      // (d) multipliers of the rows now below position k (IEEE division);
+      // column k itself keeps its values (the U entries of the rows above)
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
-        const bool below = lab[K] > k;
         const Real l = a[K][k] / d;
-        if (below) a[K][k] = l;
-        negl[i][K] = below ? -l : Real(0);
+        lm[i][K] = lab[K] > k ? l : Real(0);
       });
     });
 
@@ -419,8 +465,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int e = decltype(ec)::value;
         if constexpr (e < NT) return a[K][k0 + bw + e];
         else if constexpr (e < W) return y[K][e - NT];
-        else if constexpr (e < RECN) return a[K][k0 + e - W];
-        else return Real(0);
+        else return lm[e - W][K];
       };
       // The owner of each pivot row writes its record (exec-masked: an LDS
       // write costs the same whatever the number of active lanes), one
@@ -452,10 +497,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int j = decltype(jc)::value;
         sfor<0, j>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
-          const Real lm = rec[j * S::REC_STRIDE + W + m];
+          const Real lmj = rec[j * S::REC_STRIDE + W + m];
           sfor<0, NU>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            u[j][r] = __builtin_fma(-lm, u[m][r], u[j][r]);
+            u[j][r] = __builtin_fma(-lmj, u[m][r], u[j][r]);
           });
         });
       });
@@ -468,10 +513,11 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           constexpr int m = decltype(mc)::value;
           sfor<0, R>([&](auto Kc) {
             constexpr int K = decltype(Kc)::value;
+            constexpr bool first = (L == 0) && (K == 0);
             if constexpr (e < NT)
-              fmac_bcast<T, L>(a[K][k0 + bw + e], u[m][r], negl[m][K]);
+              fnmac_bcast<T, L, first>(a[K][k0 + bw + e], u[m][r], lm[m][K]);
             else
-              fmac_bcast<T, L>(y[K][e - NT], u[m][r], negl[m][K]);
+              fnmac_bcast<T, L, first>(y[K][e - NT], u[m][r], lm[m][K]);
           });
         });
       });
@@ -479,61 +525,103 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
   });
 
-  // ---- back substitution: x_k = y_k / u_kk on the owner of position k,
-  // fetched by the group, folded into the rows above k.  Each step is fenced
-  // off from the next in the schedule: the compiler would otherwise form the
-  // masked U entries of every step at once and run out of registers.
-  __builtin_amdgcn_sched_barrier(0);
-  sfor<0, N>([&](auto ic) {
-    constexpr int k = N - 1 - decltype(ic)::value;
-    const uint32_t code = (own[k / 4] >> (8 * (k % 4))) & 0xffu;
-    const int ol = gbase + (int)(code % T);
-    const int os = (int)(code / T);
-    Real dk = a[0][k];
-    sfor<1, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      dk = os == K ? a[K][k] : dk;
-    });
+  // ---- back substitution.  Every row, whatever lane holds it, writes its U
+  // entries (columns from its position on) and its right-hand sides to the
+  // packed triangular store at its position; then lane tx reads back the
+  // rows of positions tx + K*T, and the solve runs on fixed positions: x_k is
+  // formed by lane k % T (slot k / T), stored, and broadcast to the rows
+  // above by DPP inside the FMA.
+  auto urow = [](int q) { return q * (N + NRHS) - q * (q - 1) / 2; };  // row q offset
+  wave_sync_lds();  // the last records have been read
+  Real* ut = rec;   // the group's LDS area, now the triangular store
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    const int q = lab[K];
+    if (q >= 0) {
+      Real* row = ut + urow(q) - q;   // entry of column c at row[c]
+      sfor<0, N>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if (c >= q) row[c] = a[K][c];
+      });
+      sfor<0, NRHS>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        row[N + j] = y[K][j];
+      });
+    }
+  });
+  wave_sync_lds();
+  const bool failed = status != 0;
+  const int64_t nbx = (int64_t)n * nrhs;
+  Real* Xs = X + (live ? sys : 0) * nbx;
+  const Real* urw[R];
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    const int q = tx + K * T;
+    const int qq = q < N ? q : N - 1;
+    urw[K] = ut + urow(qq) - qq;
     sfor<0, NRHS>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      Real yk = y[0][j];
-      sfor<1, R>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        yk = os == K ? y[K][j] : yk;
-      });
-      const Real xk = lane_fetch<T>(yk / dk, ol);
-      sfor<0, R>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        const Real upd = __builtin_fma(-a[K][k], xk, y[K][j]);
-        y[K][j] = lab[K] < k ? upd : (lab[K] == k ? xk : y[K][j]);
-      });
+      y[K][j] = urw[K][N + j];
     });
-    __builtin_amdgcn_sched_barrier(0);
   });
-
-  // ---- store: X in B's layout (row of label q), piv, info
-  if (live) {
-    const int64_t nb = (int64_t)n * nrhs;
-    Real* Xs = X + sys * nb;
-    int32_t* Ps = piv + sys * (int64_t)n;
-    const bool failed = status != 0;
-    sfor<0, R>([&](auto Kc) {
+  sfor<0, N>([&](auto ic) {
+    constexpr int k = N - 1 - decltype(ic)::value;
+    constexpr int kl = k % T;
+    constexpr int ks = k / T;
+    constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
+    Real uk[ks + 1];
+    sfor<0, ks + 1>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
-      const int r = lab[K];
-      if (r >= 0 && r < n) {
-        sfor<0, NRHS>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          if (j < nrhs) {
-            const Real v = failed ? Real(0) : y[K][j];
-            if (col)
-              Xs[(int64_t)j * n + r] = v;
-            else
-              Xs[(int64_t)r * nrhs + j] = v;
-          }
+      uk[K] = urw[K][k];   // u(q, k) of this lane's row q in slot K
+    });
+    const bool owner = tx == kl && live && !failed && k < n;
+    sfor<0, NRHS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const Real x = y[ks][j] / uk[ks];   // meaningful on lane kl
+      if (owner && j < nrhs) {
+        if (col)
+          Xs[(int64_t)j * n + k] = x;
+        else
+          Xs[(int64_t)k * nrhs + j] = x;
+      }
+      // rows above k take x_k (rows at k and below are done: their updates
+      // are never read)
+      if constexpr (T <= 16) {
+        sfor<0, ks + 1>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          fnmac_bcast<T, SLK, K == 0>(y[K][j], x, uk[K]);
+        });
+      } else {
+        // x_k lives in one lane of one 16-lane row: fetch it for the group
+        const Real xk = lane_fetch<T>(x, gbase + kl);
+        sfor<0, ks + 1>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          y[K][j] = __builtin_fma(-uk[K], xk, y[K][j]);
         });
       }
+    });
+  });
+
+  // ---- store: piv, info, and the zero solution of a failed system
+  if (live) {
+    int32_t* Ps = piv + sys * (int64_t)n;
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
       const int q = tx + K * T;
-      if (q < n) Ps[q] = failed ? -1 : pv[K];
+      if (q < n) {
+        if (failed) {
+          sfor<0, NRHS>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if (j < nrhs) {
+              if (col)
+                Xs[(int64_t)j * n + q] = Real(0);
+              else
+                Xs[(int64_t)q * nrhs + j] = Real(0);
+            }
+          });
+        }
+        Ps[q] = failed ? -1 : pv[K];
+      }
     });
     if (tx == 0) info[sys] = status;
   }

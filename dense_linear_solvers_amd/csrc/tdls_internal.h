@@ -80,14 +80,17 @@ constexpr int panel_width(int N, [[maybe_unused]] int NRHS, [[maybe_unused]] boo
   return N < 4 ? N : 4;
 }
 
-// LDS bytes of one block: per wave, G groups x B records of N + NRHS entries
-// (rounded up to 16 bytes).
+// LDS bytes of one block: per wave and group, the larger of B records of
+// N + NRHS entries (rounded up to 16 bytes) and the packed upper-triangular
+// store of U with the right-hand sides used by the back substitution.
 constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
   const int es = is64 ? 8 : 4;
   const int vec = 16 / es;
   const int stride = (N + NRHS + vec - 1) / vec * vec;
   const int B = panel_width(N, NRHS, is64);
-  return kWavesPerBlock * (kWaveSize / T) * B * stride * es;
+  const int utri = (N * (N + NRHS) - N * (N - 1) / 2 + vec - 1) / vec * vec;
+  const int group = B * stride > utri ? B * stride : utri;
+  return kWavesPerBlock * (kWaveSize / T) * group * es;
 }
 
 // Launchers, one per shape of TDLS_FOR_EACH_SHAPE, defined in the
