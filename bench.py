@@ -262,6 +262,7 @@ def main():
         "config": {"workload": w.name, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
                    "layout": "column-major" if w.layout == "col" else "row-major",
                    "distribution": w.meta.get("recipe"), "seed": 0,
+                   **({"gap_filtered": False} if "gap_filtered" in w.meta else {}),
                    "group_size": plan["group_size"], "systems_per_wave": plan["systems_per_wave"]},
         "kernel_ms": kernel_ms,
         "hbm_gbs_algorithmic": achieved_gbs,
