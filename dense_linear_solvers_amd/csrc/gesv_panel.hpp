@@ -126,30 +126,41 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
   return v;
 }
 
-// True, uniformly over the wave, when some group has more than one lane with
-// `pred` set.
-template <int T>
-__device__ __forceinline__ bool group_tie(bool pred) {
-  const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+// Lane of the group that wins the pivot search.  `top` marks the lanes whose
+// flagged high word equals the group maximum, `lo` their low word (float64)
+// and `key` their position key.  A ballot names the winner when each group
+// has a single top lane (the common case); otherwise, uniformly over the
+// wave, the low word and then the lowest key decide among the top lanes.
+// Every group always has a candidate (the rows at positions >= k), so the
+// ballot field of each group is never empty.
+template <int T, bool IS64>
+__device__ __forceinline__ int group_winner(bool top, uint32_t lo, uint32_t key, int gbase) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(top);
   if constexpr (T == 64) {
-    return __builtin_popcountll(m) > 1;
-  } else if constexpr (T == 32) {
-    return __builtin_popcount((uint32_t)m) > 1 || __builtin_popcount((uint32_t)(m >> 32)) > 1;
-  } else if constexpr (T == 16) {
-    bool tie = false;
-    sfor<0, 4>([&](auto gc) {
-      constexpr int gi = decltype(gc)::value;
-      tie = tie || __builtin_popcount((uint32_t)(m >> (16 * gi)) & 0xffffu) > 1;
-    });
-    return tie;
+    if (__builtin_popcountll(m) == 1) return __builtin_ctzll(m);
   } else {
-    // lanes 4g..4g+3: a set pair inside a quad shows in (m & m >> 1), (m & m >> 2)
-    // or (m & m >> 3) at a bit whose quad offset keeps both bits in the quad
-    const uint64_t m1 = m & (m >> 1) & 0x7777777777777777ull;
-    const uint64_t m2 = m & (m >> 2) & 0x3333333333333333ull;
-    const uint64_t m3 = m & (m >> 3) & 0x1111111111111111ull;
-    return (m1 | m2 | m3) != 0;
+    constexpr uint32_t GM = T == 32 ? 0xffffffffu : ((1u << T) - 1u);
+    const uint32_t fld = (uint32_t)(m >> gbase) & GM;
+    const bool multi = (fld & (fld - 1u)) != 0u;
+    if (__builtin_amdgcn_ballot_w64(multi) == 0) return gbase + __builtin_ctz(fld);
   }
+  bool t = top;
+  if constexpr (IS64) {
+    const uint32_t ml = group_reduce<T, true>(t ? lo : 0u);
+    t = t & (lo == ml);
+  }
+  const uint32_t kmin = group_reduce<T, false>(t ? key : 0xffffffffu);
+  return (int)((kmin >> 5) & 63u);
+}
+
+// 32-bit value of `x` held by lane `src` (absolute lane index) of this wave;
+// `src` is wave-uniform when T = 64.
+template <int T>
+__device__ __forceinline__ uint32_t lane_fetch_u32(uint32_t x, int src) {
+  if constexpr (T == 64)
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, __builtin_amdgcn_readfirstlane(src));
+  else
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)x);
 }
 
 // Value of `x` held by lane `src` (absolute lane index) of this wave.
@@ -235,9 +246,6 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
-
-__device__ __forceinline__ float absr(float v) { return __builtin_fabsf(v); }
-__device__ __forceinline__ double absr(double v) { return __builtin_fabs(v); }
 
 __device__ __forceinline__ uint32_t hi_word(double v) {
   return (uint32_t)(__builtin_bit_cast(uint64_t, v) >> 32);
@@ -391,48 +399,64 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         });
       });
 
-      // (b) pivot search on column k over the rows at positions >= k.  Each
-      // lane keeps its best slot (larger |a|, then lower position); the
-      // group takes the largest leading word of |a|; only when two lanes
-      // share it (rare, uniform branch) is the trailing word compared; the
-      // lowest position among the remaining ties wins.
-      Real cv = a[0][k];
-      uint32_t ck = kb[0];
-      bool cact = lab[0] >= k;
-      sfor<1, R>([&](auto Kc) {
+      // (b) pivot search on column k over the rows at positions >= k.
+      // Candidates are compared as integers: the high word of |a| with bit
+      // 31 set for a row at a position >= k (0 for the others), then the low
+      // word (float64), then the key (lower position wins).  Each lane keeps
+      // its best slot without branches; the group takes the largest flagged
+      // high word by DPP.  Usually one lane holds it and a ballot names that
+      // lane; when several lanes of some group share it (a uniform, rare
+      // branch), the low word and then the key decide by two more passes.
+      uint32_t bh = 0, bl = 0, bk = 0;
+      sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
-        const bool act = lab[K] >= k;
-        const Real v = a[K][k];
-        const bool better = absr(v) > absr(cv) || (absr(v) == absr(cv) && kb[K] < ck);
-        const bool take = act && (!cact || better);
-        cv = take ? v : cv;
-        ck = take ? kb[K] : ck;
-        cact = cact || act;
-      });
-      uint32_t chi;
-      if constexpr (is64)
-        chi = hi_word(cv);
-      else
-        chi = __builtin_bit_cast(uint32_t, cv);
-      const uint32_t sgn = chi >> 31;
-      chi = cact ? (chi | 0x80000000u) : 0u;  // top bit: candidate; rest: |a| bits
-      const uint32_t mhi = group_reduce<T, true>(chi);
-      bool top = chi == mhi && cact;
-      if constexpr (is64) {
-        if (group_tie<T>(top)) {
-          const uint32_t clo = top ? lo_word(cv) : 0u;
-          const uint32_t mlo = group_reduce<T, true>(clo);
-          top = top && lo_word(cv) == mlo;
+        uint32_t h, l = 0;
+        if constexpr (is64) {
+          h = hi_word(a[K][k]);
+          l = lo_word(a[K][k]);
+        } else {
+          h = __builtin_bit_cast(uint32_t, a[K][k]);
         }
-      }
-      const uint32_t kmin = group_reduce<T, false>(top ? (ck | sgn) : 0xffffffffu);
-      const bool any = kmin != 0xffffffffu;
-      const int p = any ? (int)(kmin >> 13) : k;
-      const int ol = any ? (int)((kmin >> 5) & 63u) : gbase + kl;
-      const int os = any ? (int)((kmin >> 1) & 15u) : ks;
-      const Real dpiv = lane_fetch<T>(cv, ol);  // the winner's own candidate
-      const bool zero_pivot = !any || dpiv == Real(0);
+        const uint32_t hf = lab[K] >= k ? (h | 0x80000000u) : 0u;
+        const uint32_t kk = kb[K] | (h >> 31);
+        if constexpr (K == 0) {
+          bh = hf;
+          bl = l;
+          bk = kk;
+        } else {
+          bool take;
+          if constexpr (is64) {
+            const uint64_t c = ((uint64_t)hf << 32) | l;
+            const uint64_t b = ((uint64_t)bh << 32) | bl;
+            take = (c > b) | ((c == b) & (kk < bk));
+          } else {
+            take = (hf > bh) | ((hf == bh) & (kk < bk));
+          }
+          bh = take ? hf : bh;
+          bl = take ? l : bl;
+          bk = take ? kk : bk;
+        }
+      });
+      // every group has a candidate, so mh has bit 31 set and only flagged
+      // lanes can equal it
+      const uint32_t mh = group_reduce<T, true>(bh);
+      const bool top = bh == mh;
+      const int wl = group_winner<T, is64>(top, bl, bk, gbase);
+      const uint32_t wk = lane_fetch_u32<T>(bk, wl);      // winner's key and sign
+      const int p = (int)(wk >> 13);
+      const int ol = wl;
+      const int os = (int)((wk >> 1) & 15u);
+      const uint32_t dh = (mh & 0x7fffffffu) | (wk << 31);
+      Real dpiv;
+      if constexpr (is64)
+        dpiv = __builtin_bit_cast(double, ((uint64_t)dh << 32) | lane_fetch_u32<T>(bl, wl));
+      else
+        dpiv = __builtin_bit_cast(float, dh);
+      const bool zero_pivot = dpiv == Real(0);
       if (zero_pivot && status == 0) status = k + 1;
+      // settle the status here: left to the end, the per-step zero flags of
+      // every step stay live in scalar registers
+      asm volatile("" : "+v"(status));
       const Real d = zero_pivot ? Real(1) : dpiv;
 
       // (c) logical interchange of positions k and p
@@ -446,6 +470,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       ownl[i] = ol;
       owns[i] = os;
       if (tx == kl) pv[ks] = p;
+      asm volatile("" : "+v"(pv[ks]));   // likewise for the pivot record
 
       // (d) multipliers of the rows now below position k (IEEE division);
       // column k itself keeps its values (the U entries of the rows above)
@@ -551,8 +576,6 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   });
   wave_sync_lds();
   const bool failed = status != 0;
-  const int64_t nbx = (int64_t)n * nrhs;
-  Real* Xs = X + (live ? sys : 0) * nbx;
   const Real* urw[R];
   sfor<0, R>([&](auto Kc) {
     constexpr int K = decltype(Kc)::value;
@@ -564,26 +587,31 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       y[K][j] = urw[K][N + j];
     });
   });
+  // x of the positions tx + K*T, kept by this lane until the final store
+  // (every entry is assigned at its own step; the zeros are never stored)
+  Real xr[R][NRHS];
+  sfor<0, R>([&](auto Kc) {
+    sfor<0, NRHS>([&](auto jc) { xr[decltype(Kc)::value][decltype(jc)::value] = Real(0); });
+  });
   sfor<0, N>([&](auto ic) {
     constexpr int k = N - 1 - decltype(ic)::value;
     constexpr int kl = k % T;
     constexpr int ks = k / T;
     constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
+    // keep the U reads of one step together with their use (hoisting them
+    // all ahead of the loop costs registers, not latency)
+    __builtin_amdgcn_sched_barrier(0);
     Real uk[ks + 1];
     sfor<0, ks + 1>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
       uk[K] = urw[K][k];   // u(q, k) of this lane's row q in slot K
     });
-    const bool owner = tx == kl && live && !failed && k < n;
+    const bool owner = tx == kl;
     sfor<0, NRHS>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const Real x = y[ks][j] / uk[ks];   // meaningful on lane kl
-      if (owner && j < nrhs) {
-        if (col)
-          Xs[(int64_t)j * n + k] = x;
-        else
-          Xs[(int64_t)k * nrhs + j] = x;
-      }
+      xr[ks][j] = owner ? x : xr[ks][j];
+      asm volatile("" : "+v"(xr[ks][j]));   // select now, not at the store
       // rows above k take x_k (rows at k and below are done: their updates
       // are never read)
       if constexpr (T <= 16) {
@@ -602,24 +630,24 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     });
   });
 
-  // ---- store: piv, info, and the zero solution of a failed system
+  // ---- store: X (all +0.0 for a failed system), piv (all -1), info
   if (live) {
+    Real* Xs = X + sys * ((int64_t)n * nrhs);
     int32_t* Ps = piv + sys * (int64_t)n;
     sfor<0, R>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
       const int q = tx + K * T;
       if (q < n) {
-        if (failed) {
-          sfor<0, NRHS>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            if (j < nrhs) {
-              if (col)
-                Xs[(int64_t)j * n + q] = Real(0);
-              else
-                Xs[(int64_t)q * nrhs + j] = Real(0);
-            }
-          });
-        }
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if (j < nrhs) {
+            const Real v = failed ? Real(0) : xr[K][j];
+            if (col)
+              Xs[(int64_t)j * n + q] = v;
+            else
+              Xs[(int64_t)q * nrhs + j] = v;
+          }
+        });
         Ps[q] = failed ? -1 : pv[K];
       }
     });
