@@ -126,33 +126,6 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
   return v;
 }
 
-// Lane of the group that wins the pivot search.  `top` marks the lanes whose
-// flagged high word equals the group maximum, `lo` their low word (float64)
-// and `key` their position key.  A ballot names the winner when each group
-// has a single top lane (the common case); otherwise, uniformly over the
-// wave, the low word and then the lowest key decide among the top lanes.
-// Every group always has a candidate (the rows at positions >= k), so the
-// ballot field of each group is never empty.
-template <int T, bool IS64>
-__device__ __forceinline__ int group_winner(bool top, uint32_t lo, uint32_t key, int gbase) {
-  const uint64_t m = __builtin_amdgcn_ballot_w64(top);
-  if constexpr (T == 64) {
-    if (__builtin_popcountll(m) == 1) return __builtin_ctzll(m);
-  } else {
-    constexpr uint32_t GM = T == 32 ? 0xffffffffu : ((1u << T) - 1u);
-    const uint32_t fld = (uint32_t)(m >> gbase) & GM;
-    const bool multi = (fld & (fld - 1u)) != 0u;
-    if (__builtin_amdgcn_ballot_w64(multi) == 0) return gbase + __builtin_ctz(fld);
-  }
-  bool t = top;
-  if constexpr (IS64) {
-    const uint32_t ml = group_reduce<T, true>(t ? lo : 0u);
-    t = t & (lo == ml);
-  }
-  const uint32_t kmin = group_reduce<T, false>(t ? key : 0xffffffffu);
-  return (int)((kmin >> 5) & 63u);
-}
-
 // 32-bit value of `x` held by lane `src` (absolute lane index) of this wave;
 // `src` is wave-uniform when T = 64.
 template <int T>
@@ -298,21 +271,32 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     const Real* As = A + (live ? sys : 0) * (int64_t)n * n;
     const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
     if (n == N && nrhs == NRHS) {
+      // Loads are issued column by column over the slots, so the first
+      // pivot search waits only for the first column to arrive while the
+      // rest of the tile streams in behind it.
       auto load_exact = [&](auto colc) {
         constexpr bool COL = decltype(colc)::value;
+        const Real* ar[R];
+        const Real* br[R];
         sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
           const int q = tx + K * T;
           const int qq = q < N ? q : 0;
-          const Real* ar = As + (COL ? qq : qq * N);
-          const Real* br = Bs + (COL ? qq : qq * NRHS);
-          sfor<0, N>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            a[K][c] = ar[COL ? c * N : c];
+          ar[K] = As + (COL ? qq : qq * N);
+          br[K] = Bs + (COL ? qq : qq * NRHS);
+        });
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          sfor<0, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            a[K][c] = ar[K][COL ? c * N : c];
           });
-          sfor<0, NRHS>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            y[K][j] = br[COL ? j * N : j];
+        });
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          sfor<0, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            y[K][j] = br[K][COL ? j * N : j];
           });
         });
       };
@@ -375,83 +359,116 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     constexpr int NT = N - k0 - bw;                    // trailing matrix columns
     constexpr int W = NT + NRHS;                       // trailing entries per row
     Real lm[B][R];                                     // multiplier, 0 unless below
-    int ownl[B];                                       // owning lane (absolute) of pivot i
-    int owns[B];                                       // and its slot
 
     sfor<0, bw>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int k = k0 + i;
       constexpr int kl = k % T;
       constexpr int ks = k / T;
-
-      // (a) column k takes the updates of this panel's earlier pivots, in order
-      sfor<0, i>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        Real sel = a[0][k];
-        sfor<1, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          sel = owns[m] == K ? a[K][k] : sel;
-        });
-        const Real um = lane_fetch<T>(sel, ownl[m]);
-        sfor<0, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          a[K][k] = __builtin_fma(-lm[m][K], um, a[K][k]);
-        });
-      });
+      constexpr int PC = bw - 1 - i;   // panel columns right of k
 
       // (b) pivot search on column k over the rows at positions >= k.
-      // Candidates are compared as integers: the high word of |a| with bit
-      // 31 set for a row at a position >= k (0 for the others), then the low
-      // word (float64), then the key (lower position wins).  Each lane keeps
-      // its best slot without branches; the group takes the largest flagged
-      // high word by DPP.  Usually one lane holds it and a ballot names that
-      // lane; when several lanes of some group share it (a uniform, rare
-      // branch), the low word and then the key decide by two more passes.
-      uint32_t bh = 0, bl = 0, bk = 0;
+      // Candidates compare as integers: the high word of |a| with bit 31 set
+      // for a row at a position >= k (0 for the others), then the low word
+      // (float64), then the position.  The group maximum of the flagged
+      // high words comes from a DPP max over each lane's largest slot; the
+      // slots that hold it are balloted.  When every group has exactly one
+      // (the common case, decided uniformly) that slot wins and its lane is
+      // the group's set ballot bit.  Otherwise each lane picks its best slot
+      // exactly and the low word, then the lowest position, decide among
+      // the lanes that hold the maximum.
+      uint32_t hw[R], lw[R], hf[R];
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
-        uint32_t h, l = 0;
         if constexpr (is64) {
-          h = hi_word(a[K][k]);
-          l = lo_word(a[K][k]);
+          hw[K] = hi_word(a[K][k]);
+          lw[K] = lo_word(a[K][k]);
         } else {
-          h = __builtin_bit_cast(uint32_t, a[K][k]);
+          hw[K] = __builtin_bit_cast(uint32_t, a[K][k]);
+          lw[K] = 0u;
         }
-        const uint32_t hf = lab[K] >= k ? (h | 0x80000000u) : 0u;
-        const uint32_t kk = kb[K] | (h >> 31);
-        if constexpr (K == 0) {
-          bh = hf;
-          bl = l;
-          bk = kk;
-        } else {
-          bool take;
-          if constexpr (is64) {
-            const uint64_t c = ((uint64_t)hf << 32) | l;
-            const uint64_t b = ((uint64_t)bh << 32) | bl;
-            take = (c > b) | ((c == b) & (kk < bk));
-          } else {
-            take = (hf > bh) | ((hf == bh) & (kk < bk));
-          }
-          bh = take ? hf : bh;
-          bl = take ? l : bl;
-          bk = take ? kk : bk;
-        }
+        hf[K] = lab[K] >= k ? (hw[K] | 0x80000000u) : 0u;
+      });
+      uint32_t lmax = hf[0];
+      sfor<1, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        lmax = lmax > hf[K] ? lmax : hf[K];
       });
       // every group has a candidate, so mh has bit 31 set and only flagged
-      // lanes can equal it
-      const uint32_t mh = group_reduce<T, true>(bh);
-      const bool top = bh == mh;
-      const int wl = group_winner<T, is64>(top, bl, bk, gbase);
-      const uint32_t wk = lane_fetch_u32<T>(bk, wl);      // winner's key and sign
+      // slots can equal it
+      const uint32_t mh = group_reduce<T, true>(lmax);
+      bool tp[R];
+      uint64_t tmask = 0;
+      int ntop = 0;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        tp[K] = hf[K] == mh;
+        const uint64_t b = __builtin_amdgcn_ballot_w64(tp[K]);
+        tmask |= b;
+        ntop += __builtin_popcountll(b);
+      });
+      // The lane's chosen slot (its top slot, or its best one when the
+      // exact comparison runs): its key, value and entries right of k in the
+      // panel are what the winning lane hands to its group.
+      uint32_t ch = hw[0], cl = lw[0], ck = kb[0];
+      Real cpan[PC > 0 ? PC : 1];
+      sfor<0, PC>([&](auto cc) { cpan[decltype(cc)::value] = a[0][k + 1 + decltype(cc)::value]; });
+      auto choose = [&](auto Kc, bool take) {
+        constexpr int K = decltype(Kc)::value;
+        ch = take ? hw[K] : ch;
+        cl = take ? lw[K] : cl;
+        ck = take ? kb[K] : ck;
+        sfor<0, PC>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          cpan[c] = take ? a[K][k + 1 + c] : cpan[c];
+        });
+      };
+      int wl;   // winning lane
+      if (__builtin_expect(ntop == G, 1)) {
+        sfor<1, R>([&](auto Kc) { choose(Kc, tp[decltype(Kc)::value]); });
+        if constexpr (T == 64) {
+          wl = __builtin_ctzll(tmask);
+        } else {
+          constexpr uint32_t GM = T == 32 ? 0xffffffffu : ((1u << T) - 1u);
+          wl = gbase + __builtin_ctz((uint32_t)(tmask >> gbase) & GM);
+        }
+      } else {
+        uint32_t bh = hf[0], bl = lw[0];
+        sfor<1, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          bool take;
+          if constexpr (is64) {
+            const uint64_t c = ((uint64_t)hf[K] << 32) | lw[K];
+            const uint64_t bb = ((uint64_t)bh << 32) | bl;
+            take = (c > bb) | ((c == bb) & (kb[K] < ck));
+          } else {
+            take = (hf[K] > bh) | ((hf[K] == bh) & (kb[K] < ck));
+          }
+          bh = take ? hf[K] : bh;
+          bl = take ? lw[K] : bl;
+          choose(Kc, take);
+        });
+        bool top = bh == mh;
+        if constexpr (is64) {
+          const uint32_t ml = group_reduce<T, true>(top ? bl : 0u);
+          top = top & (bl == ml);
+        }
+        const uint32_t kmin = group_reduce<T, false>(top ? ck : 0xffffffffu);
+        wl = (int)((kmin >> 5) & 63u);
+      }
+      const uint32_t wk = lane_fetch_u32<T>(ck, wl);      // winner's key
       const int p = (int)(wk >> 13);
-      const int ol = wl;
-      const int os = (int)((wk >> 1) & 15u);
-      const uint32_t dh = (mh & 0x7fffffffu) | (wk << 31);
+      Real upan[PC > 0 ? PC : 1];                          // pivot row, right of k
+      sfor<0, PC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        upan[c] = lane_fetch<T>(cpan[c], wl);
+      });
       Real dpiv;
       if constexpr (is64)
-        dpiv = __builtin_bit_cast(double, ((uint64_t)dh << 32) | lane_fetch_u32<T>(bl, wl));
+        dpiv = __builtin_bit_cast(double, ((uint64_t)lane_fetch_u32<T>(ch, wl) << 32) |
+                                              lane_fetch_u32<T>(cl, wl));
       else
-        dpiv = __builtin_bit_cast(float, dh);
+        dpiv = __builtin_bit_cast(float, lane_fetch_u32<T>(ch, wl));
       const bool zero_pivot = dpiv == Real(0);
       if (zero_pivot && status == 0) status = k + 1;
       // settle the status here: left to the end, the per-step zero flags of
@@ -467,8 +484,6 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         lab[K] = nl;
         kb[K] = (kb[K] & 0x1fffu) | ((uint32_t)(nl < 0 ? 0 : nl) << 13);
       });
-      ownl[i] = ol;
-      owns[i] = os;
       if (tx == kl) pv[ks] = p;
       asm volatile("" : "+v"(pv[ks]));   // likewise for the pivot record
 
@@ -478,6 +493,15 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int K = decltype(Kc)::value;
         const Real l = a[K][k] / d;
         lm[i][K] = lab[K] > k ? l : Real(0);
+      });
+      // (e) the rest of the panel takes this pivot's update now, so the next
+      // column is complete when its search starts
+      sfor<0, PC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          a[K][k + 1 + c] = __builtin_fma(-lm[i][K], upan[c], a[K][k + 1 + c]);
+        });
       });
     });
 
