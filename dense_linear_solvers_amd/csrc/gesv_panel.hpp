@@ -126,6 +126,17 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
   return v;
 }
 
+// Value of `x` held by lane `src` (absolute lane index, may differ per lane).
+__device__ __forceinline__ double lane_fetch_any(double x, int src) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float lane_fetch_any(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
 // 32-bit value of `x` held by lane `src` (absolute lane index) of this wave;
 // `src` is wave-uniform when T = 64.
 template <int T>
@@ -600,80 +611,143 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   });
   wave_sync_lds();
   const bool failed = status != 0;
-  const Real* urw[R];
-  sfor<0, R>([&](auto Kc) {
-    constexpr int K = decltype(Kc)::value;
-    const int q = tx + K * T;
-    const int qq = q < N ? q : N - 1;
-    urw[K] = ut + urow(qq) - qq;
-    sfor<0, NRHS>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      y[K][j] = urw[K][N + j];
-    });
-  });
-  // x of the positions tx + K*T, kept by this lane until the final store
-  // (every entry is assigned at its own step; the zeros are never stored)
-  Real xr[R][NRHS];
-  sfor<0, R>([&](auto Kc) {
-    sfor<0, NRHS>([&](auto jc) { xr[decltype(Kc)::value][decltype(jc)::value] = Real(0); });
-  });
-  sfor<0, N>([&](auto ic) {
-    constexpr int k = N - 1 - decltype(ic)::value;
-    constexpr int kl = k % T;
-    constexpr int ks = k / T;
-    constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
-    // keep the U reads of one step together with their use (hoisting them
-    // all ahead of the loop costs registers, not latency)
-    __builtin_amdgcn_sched_barrier(0);
-    Real uk[ks + 1];
-    sfor<0, ks + 1>([&](auto Kc) {
+  int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
+  Real* Xs = X + (live ? sys : 0) * ((int64_t)n * nrhs);
+
+  if constexpr (NRHS == 1) {
+    // One right-hand side: lane tx reads back the rows of positions
+    // tx + K*T; x_k is formed by lane k % T (slot k / T) and reaches the rows
+    // above by DPP inside the FMA (a lane fetch for groups wider than a
+    // 16-lane row).
+    const Real* urw[R];
+    Real yv[R];
+    sfor<0, R>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
-      uk[K] = urw[K][k];   // u(q, k) of this lane's row q in slot K
+      const int q = tx + K * T;
+      const int qq = q < N ? q : N - 1;
+      urw[K] = ut + urow(qq) - qq;
+      yv[K] = urw[K][N];
     });
-    const bool owner = tx == kl;
-    sfor<0, NRHS>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const Real x = y[ks][j] / uk[ks];   // meaningful on lane kl
-      xr[ks][j] = owner ? x : xr[ks][j];
-      asm volatile("" : "+v"(xr[ks][j]));   // select now, not at the store
+    // x of the positions tx + K*T, kept by this lane until the final store
+    // (every entry is assigned at its own step)
+    Real xr[R];
+    sfor<0, R>([&](auto Kc) { xr[decltype(Kc)::value] = Real(0); });
+    sfor<0, N>([&](auto ic) {
+      constexpr int k = N - 1 - decltype(ic)::value;
+      constexpr int kl = k % T;
+      constexpr int ks = k / T;
+      constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
+      // keep the U reads of one step together with their use (hoisting them
+      // all ahead of the loop costs registers, not latency)
+      __builtin_amdgcn_sched_barrier(0);
+      Real uk[ks + 1];
+      sfor<0, ks + 1>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        uk[K] = urw[K][k];   // u(q, k) of this lane's row q in slot K
+      });
+      const Real x = yv[ks] / uk[ks];   // meaningful on lane kl
+      xr[ks] = tx == kl ? x : xr[ks];
+      asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
       // rows above k take x_k (rows at k and below are done: their updates
       // are never read)
       if constexpr (T <= 16) {
         sfor<0, ks + 1>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          fnmac_bcast<T, SLK, K == 0>(y[K][j], x, uk[K]);
+          fnmac_bcast<T, SLK, K == 0>(yv[K], x, uk[K]);
         });
       } else {
-        // x_k lives in one lane of one 16-lane row: fetch it for the group
         const Real xk = lane_fetch<T>(x, gbase + kl);
         sfor<0, ks + 1>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          y[K][j] = __builtin_fma(-uk[K], xk, y[K][j]);
+          yv[K] = __builtin_fma(-uk[K], xk, yv[K]);
         });
       }
     });
-  });
-
-  // ---- store: X (all +0.0 for a failed system), piv (all -1), info
-  if (live) {
-    Real* Xs = X + sys * ((int64_t)n * nrhs);
-    int32_t* Ps = piv + sys * (int64_t)n;
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      if (q < n) {
-        sfor<0, NRHS>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          if (j < nrhs) {
-            const Real v = failed ? Real(0) : xr[K][j];
+    if (live) {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        if (q < n) Xs[q] = failed ? Real(0) : xr[K];   // one column: same address in both layouts
+      });
+    }
+  } else {
+    // Several right-hand sides: the group's lanes split into NJ column
+    // classes and P row phases.  Lane (ph, j0) holds the right-hand-side
+    // columns j = j0 + NJ*jj of the positions q = ph + P*m, so each x_k is
+    // one division per column on the NJ lanes of phase k % P, handed to the
+    // lanes of the same column class by a lane fetch; every lane then folds
+    // it into its rows, reading u(q, k) from the triangular store.
+    constexpr int NJ = NRHS < T ? NRHS : T;
+    constexpr int P = T / NJ;
+    constexpr int JR = NRHS / NJ;
+    constexpr int QR = (N + P - 1) / P;
+    const int j0 = tx % NJ;
+    const int ph = tx / NJ;
+    const Real* rw[QR];
+    Real yv[QR][JR], xr[QR][JR];
+    sfor<0, QR>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      const int q = ph + P * m;
+      const int qq = q < N ? q : N - 1;
+      rw[m] = ut + urow(qq) - qq;   // entry of column c at rw[m][c]
+      sfor<0, JR>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        yv[m][jj] = rw[m][N + j0 + NJ * jj];
+        xr[m][jj] = Real(0);
+      });
+    });
+    sfor<0, N>([&](auto ic) {
+      constexpr int k = N - 1 - decltype(ic)::value;
+      constexpr int kp = k % P;
+      constexpr int km = k / P;
+      __builtin_amdgcn_sched_barrier(0);
+      Real uk[km + 1];
+      sfor<0, km + 1>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        uk[m] = rw[m][k];   // u(q, k) of row q = ph + P*m (meaningful for q <= k)
+      });
+      const int src = gbase + kp * NJ + j0;   // the lane of phase kp, same column class
+      sfor<0, JR>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        const Real x = yv[km][jj] / uk[km];   // meaningful on the lanes of phase kp
+        xr[km][jj] = ph == kp ? x : xr[km][jj];
+        asm volatile("" : "+v"(xr[km][jj]));
+        Real xk;
+        if constexpr (P == 1)
+          xk = x;   // every lane is the owner of its own column class
+        else
+          xk = lane_fetch_any(x, src);
+        sfor<0, km + 1>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          yv[m][jj] = __builtin_fma(-uk[m], xk, yv[m][jj]);
+        });
+      });
+    });
+    if (live) {
+      sfor<0, QR>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const int q = ph + P * m;
+        sfor<0, JR>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          const int j = j0 + NJ * jj;
+          if (q < n && j < nrhs) {
+            const Real v = failed ? Real(0) : xr[m][jj];
             if (col)
               Xs[(int64_t)j * n + q] = v;
             else
               Xs[(int64_t)q * nrhs + j] = v;
           }
         });
-        Ps[q] = failed ? -1 : pv[K];
-      }
+      });
+    }
+  }
+
+  // ---- piv (all -1 for a failed system) and info
+  if (live) {
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      if (q < n) Ps[q] = failed ? -1 : pv[K];
     });
     if (tx == 0) info[sys] = status;
   }
