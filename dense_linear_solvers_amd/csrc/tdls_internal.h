@@ -31,7 +31,11 @@ constexpr int kNumNrhs = 4;
 constexpr int kNrhsValues[kNumNrhs] = {1, 2, 4, 8};
 
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerBlock = 4;
+// One wave per block: waves share nothing, and the LDS a block holds is then
+// one wave's records and triangular store, so as many waves fit on a CU as
+// its 160 KiB of LDS and the register file allow (a 4-wave block of n = 64
+// float64 systems would need 81 KiB and leave one wave per SIMD).
+constexpr int kWavesPerBlock = 1;
 
 // Everything a launch needs, decided on the host before any launch.
 struct LaunchPlan {
