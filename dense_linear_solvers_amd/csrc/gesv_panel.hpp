@@ -82,12 +82,14 @@ struct PanelShape {
   static constexpr int VEC = RealTraits<Real>::VEC;
   static constexpr int REC = N + NRHS;             // largest record: panel 0
   static constexpr int REC_STRIDE = (REC + VEC - 1) / VEC * VEC;
-  // Upper-triangular store for the back substitution: row q holds columns
-  // q..N-1 then the NRHS right-hand sides, rows packed one after another.
-  static constexpr int UROW0 = N + NRHS;                    // length of row 0
-  static constexpr int UTRI = N * (N + NRHS) - N * (N - 1) / 2;
+  // Back substitution: first the right-hand sides by position (N x NRHS),
+  // then, over them, the upper-triangular store of U (row q holds columns
+  // q..N-1, rows packed one after another).
+  static constexpr int UTRI = N * (N + 1) / 2;
   static constexpr int UTRI_PAD = (UTRI + VEC - 1) / VEC * VEC;   // keep 16-byte alignment
-  static constexpr int GROUP_ELEMS = (B * REC_STRIDE > UTRI_PAD ? B * REC_STRIDE : UTRI_PAD);
+  static constexpr int YAREA = N * NRHS;
+  static constexpr int BIG1 = B * REC_STRIDE > UTRI_PAD ? B * REC_STRIDE : UTRI_PAD;
+  static constexpr int GROUP_ELEMS = BIG1 > YAREA ? BIG1 : YAREA;
   static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
   static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
 };
@@ -585,15 +587,47 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
   });
 
-  // ---- back substitution.  Every row, whatever lane holds it, writes its U
-  // entries (columns from its position on) and its right-hand sides to the
-  // packed triangular store at its position; then lane tx reads back the
-  // rows of positions tx + K*T, and the solve runs on fixed positions: x_k is
-  // formed by lane k % T (slot k / T), stored, and broadcast to the rows
-  // above by DPP inside the FMA.
-  auto urow = [](int q) { return q * (N + NRHS) - q * (q - 1) / 2; };  // row q offset
+  // ---- back substitution.  Every row, whatever lane holds it, writes its
+  // right-hand sides to the store at its position; the lanes read them back
+  // in the layout of the solve below; then every row writes its U entries
+  // (columns from its position on) over them, into the packed triangular
+  // store, which the solve reads by position.
+  auto urow = [](int q) { return q * N - q * (q - 1) / 2; };   // row q offset
   wave_sync_lds();  // the last records have been read
-  Real* ut = rec;   // the group's LDS area, now the triangular store
+  Real* ut = rec;   // the group's LDS area
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    const int q = lab[K];
+    if (q >= 0) {
+      sfor<0, NRHS>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        ut[q * NRHS + j] = y[K][j];
+      });
+    }
+  });
+  wave_sync_lds();
+  const bool failed = status != 0;
+  int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
+  Real* Xs = X + (live ? sys : 0) * ((int64_t)n * nrhs);
+  // layout of the solve (see below): one right-hand side by slots; several
+  // by column classes and row phases
+  constexpr int NJ = NRHS < T ? NRHS : T;
+  constexpr int P = NRHS == 1 ? T : T / NJ;
+  constexpr int JR = NRHS / NJ;
+  constexpr int QR = (N + P - 1) / P;
+  const int j0 = NRHS == 1 ? 0 : tx % NJ;
+  const int ph = NRHS == 1 ? tx : tx / NJ;
+  Real yv[QR][JR];
+  sfor<0, QR>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    const int q = ph + P * m;
+    const int qq = q < N ? q : N - 1;
+    sfor<0, JR>([&](auto jc) {
+      constexpr int jj = decltype(jc)::value;
+      yv[m][jj] = ut[qq * NRHS + j0 + NJ * jj];
+    });
+  });
+  wave_sync_lds();  // read before U overwrites them
   sfor<0, R>([&](auto Kc) {
     constexpr int K = decltype(Kc)::value;
     const int q = lab[K];
@@ -603,31 +637,21 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int c = decltype(cc)::value;
         if (c >= q) row[c] = a[K][c];
       });
-      sfor<0, NRHS>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        row[N + j] = y[K][j];
-      });
     }
   });
   wave_sync_lds();
-  const bool failed = status != 0;
-  int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
-  Real* Xs = X + (live ? sys : 0) * ((int64_t)n * nrhs);
+  const Real* rw[QR];
+  sfor<0, QR>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    const int q = ph + P * m;
+    const int qq = q < N ? q : N - 1;
+    rw[m] = ut + urow(qq) - qq;   // entry of column c at rw[m][c]
+  });
 
   if constexpr (NRHS == 1) {
-    // One right-hand side: lane tx reads back the rows of positions
-    // tx + K*T; x_k is formed by lane k % T (slot k / T) and reaches the rows
-    // above by DPP inside the FMA (a lane fetch for groups wider than a
-    // 16-lane row).
-    const Real* urw[R];
-    Real yv[R];
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      const int qq = q < N ? q : N - 1;
-      urw[K] = ut + urow(qq) - qq;
-      yv[K] = urw[K][N];
-    });
+    // One right-hand side: lane tx holds the positions tx + K*T; x_k is
+    // formed by lane k % T (slot k / T) and reaches the rows above by DPP
+    // inside the FMA (a lane fetch for groups wider than a 16-lane row).
     // x of the positions tx + K*T, kept by this lane until the final store
     // (every entry is assigned at its own step)
     Real xr[R];
@@ -643,9 +667,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       Real uk[ks + 1];
       sfor<0, ks + 1>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
-        uk[K] = urw[K][k];   // u(q, k) of this lane's row q in slot K
+        uk[K] = rw[K][k];   // u(q, k) of this lane's row q in slot K
       });
-      const Real x = yv[ks] / uk[ks];   // meaningful on lane kl
+      const Real x = yv[ks][0] / uk[ks];   // meaningful on lane kl
       xr[ks] = tx == kl ? x : xr[ks];
       asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
       // rows above k take x_k (rows at k and below are done: their updates
@@ -653,13 +677,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       if constexpr (T <= 16) {
         sfor<0, ks + 1>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          fnmac_bcast<T, SLK, K == 0>(yv[K], x, uk[K]);
+          fnmac_bcast<T, SLK, K == 0>(yv[K][0], x, uk[K]);
         });
       } else {
         const Real xk = lane_fetch<T>(x, gbase + kl);
         sfor<0, ks + 1>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          yv[K] = __builtin_fma(-uk[K], xk, yv[K]);
+          yv[K][0] = __builtin_fma(-uk[K], xk, yv[K][0]);
         });
       }
     });
@@ -677,24 +701,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     // one division per column on the NJ lanes of phase k % P, handed to the
     // lanes of the same column class by a lane fetch; every lane then folds
     // it into its rows, reading u(q, k) from the triangular store.
-    constexpr int NJ = NRHS < T ? NRHS : T;
-    constexpr int P = T / NJ;
-    constexpr int JR = NRHS / NJ;
-    constexpr int QR = (N + P - 1) / P;
-    const int j0 = tx % NJ;
-    const int ph = tx / NJ;
-    const Real* rw[QR];
-    Real yv[QR][JR], xr[QR][JR];
+    Real xr[QR][JR];
     sfor<0, QR>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      const int q = ph + P * m;
-      const int qq = q < N ? q : N - 1;
-      rw[m] = ut + urow(qq) - qq;   // entry of column c at rw[m][c]
-      sfor<0, JR>([&](auto jc) {
-        constexpr int jj = decltype(jc)::value;
-        yv[m][jj] = rw[m][N + j0 + NJ * jj];
-        xr[m][jj] = Real(0);
-      });
+      sfor<0, JR>([&](auto jc) { xr[decltype(mc)::value][decltype(jc)::value] = Real(0); });
     });
     sfor<0, N>([&](auto ic) {
       constexpr int k = N - 1 - decltype(ic)::value;

@@ -84,16 +84,18 @@ constexpr int panel_width(int N, [[maybe_unused]] int NRHS, [[maybe_unused]] boo
   return N < 4 ? N : 4;
 }
 
-// LDS bytes of one block: per wave and group, the larger of B records of
-// N + NRHS entries (rounded up to 16 bytes) and the packed upper-triangular
-// store of U with the right-hand sides used by the back substitution.
+// LDS bytes of one block (one wave): per group, the largest of B records of
+// N + NRHS entries (rounded up to 16 bytes), the N x NRHS right-hand sides
+// by position and the packed upper-triangular store of U used by the back
+// substitution (the last two occupy the same area one after the other).
 constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
   const int es = is64 ? 8 : 4;
   const int vec = 16 / es;
   const int stride = (N + NRHS + vec - 1) / vec * vec;
   const int B = panel_width(N, NRHS, is64);
-  const int utri = (N * (N + NRHS) - N * (N - 1) / 2 + vec - 1) / vec * vec;
-  const int group = B * stride > utri ? B * stride : utri;
+  const int utri = (N * (N + 1) / 2 + vec - 1) / vec * vec;
+  const int big1 = B * stride > utri ? B * stride : utri;
+  const int group = big1 > N * NRHS ? big1 : N * NRHS;
   return kWavesPerBlock * (kWaveSize / T) * group * es;
 }
 
