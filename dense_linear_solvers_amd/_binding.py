@@ -38,7 +38,10 @@ class Plan(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-EXPORTED = ("tdls_gesv_batched", "tdls_plan_gesv", "tdls_strerror", "tdls_version")
+EXPORTED = ("tdls_gesv_batched", "tdls_getrf_batched", "tdls_getrs_batched", "tdls_plan_gesv",
+            "tdls_plan_op", "tdls_strerror", "tdls_version")
+OP_GESV, OP_GETRF, OP_GETRS = 0, 1, 2
+_OPS = {"gesv": OP_GESV, "getrf": OP_GETRF, "getrs": OP_GETRS}
 
 
 def library_path() -> str:
@@ -62,6 +65,17 @@ def load_library():
     lib.tdls_plan_gesv.restype = ctypes.c_int
     lib.tdls_plan_gesv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int64, ctypes.POINTER(Plan)]
+    lib.tdls_getrf_batched.restype = ctypes.c_int
+    lib.tdls_getrf_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_getrs_batched.restype = ctypes.c_int
+    lib.tdls_getrs_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_plan_op.restype = ctypes.c_int
+    lib.tdls_plan_op.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int64, ctypes.POINTER(Plan)]
     lib.tdls_strerror.restype = ctypes.c_char_p
     lib.tdls_strerror.argtypes = [ctypes.c_int]
     lib.tdls_version.restype = ctypes.c_char_p
@@ -97,6 +111,36 @@ def plan_gesv(dtype: str, layout: str, n: int, nrhs: int, batch: int) -> dict:
     rc, p = tdls_plan_gesv(F64 if dtype == "f64" else F32, _LAYOUTS[layout], n, nrhs, batch)
     if rc != 0:
         raise TdlsError(rc, "tdls_plan_gesv")
+    return p.as_dict()
+
+
+def tdls_getrf_batched(dtype: int, layout: int, n: int, batch: int, A: int, LU: int, piv: int,
+                       info: int, stream: int) -> int:
+    """The C call itself, raw pointers (ints) in, return code out."""
+    return int(load_library().tdls_getrf_batched(int(dtype), int(layout), int(n), int(batch),
+                                                 A, LU, piv, info, stream))
+
+
+def tdls_getrs_batched(dtype: int, layout: int, n: int, nrhs: int, batch: int, LU: int, piv: int,
+                       B: int, X: int, stream: int) -> int:
+    """The C call itself, raw pointers (ints) in, return code out."""
+    return int(load_library().tdls_getrs_batched(int(dtype), int(layout), int(n), int(nrhs),
+                                                 int(batch), LU, piv, B, X, stream))
+
+
+def tdls_plan_op(op: int, dtype: int, layout: int, n: int, nrhs: int, batch: int):
+    """The generic planner call: returns (code, Plan)."""
+    p = Plan()
+    rc = int(load_library().tdls_plan_op(int(op), int(dtype), int(layout), int(n), int(nrhs),
+                                         int(batch), ctypes.byref(p)))
+    return rc, p
+
+
+def plan_op(op: str, dtype: str, layout: str, n: int, nrhs: int, batch: int) -> dict:
+    rc, p = tdls_plan_op(_OPS[op], F64 if dtype == "f64" else F32, _LAYOUTS[layout], n, nrhs,
+                         batch)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_plan_op")
     return p.as_dict()
 
 
@@ -147,3 +191,76 @@ def gesv_batched(A, B, layout: str = "row", out=None, stream=None):
     if rc != 0:
         raise TdlsError(rc, "tdls_gesv_batched")
     return X, piv, info
+
+
+def _check_square(torch, A, name):
+    if A.dtype not in (torch.float32, torch.float64):
+        raise TypeError(f"{name} must be float32 or float64")
+    if not A.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if not A.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if A.dim() != 3 or A.shape[1] != A.shape[2]:
+        raise ValueError(f"{name} must be [batch, n, n]")
+
+
+def getrf_batched(A, layout: str = "row", out=None, stream=None):
+    """Factor a batch of matrices held in torch CUDA tensors: P A = L U.
+
+    A: [batch, n, n] storage in ``layout``.  Returns (LU, piv, info): LU like
+    A (LAPACK's row order, unit-lower L below the diagonal, U on and above
+    it, in the same layout), piv int32 [batch, n] (0-based swap sequence, -1
+    for a failed system), info int32 [batch].  Does not synchronize.
+    """
+    torch = _torch()
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'row' or 'col'")
+    _check_square(torch, A, "A")
+    batch, n = A.shape[0], A.shape[1]
+    if out is None:
+        LU = torch.empty_like(A)
+        piv = torch.empty((batch, n), dtype=torch.int32, device=A.device)
+        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+    else:
+        LU, piv, info = out
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        rc = tdls_getrf_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
+                                batch, A.data_ptr(), LU.data_ptr(), piv.data_ptr(),
+                                info.data_ptr(), s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_getrf_batched")
+    return LU, piv, info
+
+
+def getrs_batched(LU, piv, B, layout: str = "row", out=None, stream=None):
+    """Solve from factors of getrf_batched: X with A X = B.
+
+    LU: [batch, n, n] and piv int32 [batch, n] as returned by getrf_batched
+    (same layout); B: [batch, n, nrhs] ("row") or [batch, nrhs, n] ("col").
+    Returns X shaped like B.  Does not synchronize.
+    """
+    torch = _torch()
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'row' or 'col'")
+    _check_square(torch, LU, "LU")
+    batch, n = LU.shape[0], LU.shape[1]
+    if B.dtype != LU.dtype or not B.is_cuda or B.device != LU.device or not B.is_contiguous():
+        raise ValueError("B must be a contiguous CUDA tensor of LU's dtype and device")
+    if piv.dtype != torch.int32 or piv.device != LU.device or not piv.is_contiguous() \
+            or tuple(piv.shape) != (batch, n):
+        raise ValueError("piv must be a contiguous int32 [batch, n] tensor on LU's device")
+    if B.dim() != 3 or B.shape[0] != batch:
+        raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
+    nrhs = B.shape[2] if layout == "row" else B.shape[1]
+    if (B.shape[1] if layout == "row" else B.shape[2]) != n:
+        raise ValueError("B does not match n")
+    X = torch.empty_like(B) if out is None else out
+    s = stream if stream is not None else torch.cuda.current_stream(LU.device)
+    with torch.cuda.device(LU.device):
+        rc = tdls_getrs_batched(F64 if LU.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
+                                nrhs, batch, LU.data_ptr(), piv.data_ptr(), B.data_ptr(),
+                                X.data_ptr(), s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_getrs_batched")
+    return X

@@ -3,6 +3,7 @@
 // -DTDLS_INST_N=<N> -DTDLS_INST_NRHS=<NRHS>, so that the kernels build in
 // parallel.
 #include "gesv_panel.hpp"
+#include "getrs_kernel.hpp"
 
 #if !defined(TDLS_INST_SFX) || !defined(TDLS_INST_REAL) || !defined(TDLS_INST_N) || \
     !defined(TDLS_INST_NRHS)
@@ -14,9 +15,9 @@
 
 namespace tdls {
 
-template <typename Real, int N, int NRHS, int T>
-static int launch_instance(const LaunchPlan& p, const void* A, const void* B, void* X,
-                           int32_t* piv, int32_t* info, hipStream_t stream) {
+template <typename Real, int N, int NRHS, int T, bool FACT>
+static int launch_panel(const LaunchPlan& p, const void* A, const void* B, void* X,
+                        int32_t* piv, int32_t* info, hipStream_t stream) {
   constexpr int PB = panel_width(N, NRHS, sizeof(Real) == 8);
   using S = PanelShape<Real, N, NRHS, T, PB>;
   static_assert(S::BLOCK_BYTES == gesv_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
@@ -26,20 +27,51 @@ static int launch_instance(const LaunchPlan& p, const void* A, const void* B, vo
     // Dynamic LDS above 64 KiB has to be allowed per kernel; done once (the
     // static is initialised thread-safely) and the outcome kept.
     static const hipError_t allowed = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gesv_panel_kernel<Real, N, NRHS, T, PB>),
+        reinterpret_cast<const void*>(&gesv_panel_kernel<Real, N, NRHS, T, PB, FACT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, S::BLOCK_BYTES);
     if (allowed != hipSuccess) return (int)allowed;
   }
-  hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB>), dim3((unsigned)p.grid),
+  hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB, FACT>), dim3((unsigned)p.grid),
                      dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                      p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),
                      static_cast<Real*>(X), piv, info);
   return (int)hipGetLastError();
 }
 
+template <typename Real, int N, int NRHS, int T>
+static int launch_getrs(const LaunchPlan& p, const void* LU, const void* B, void* X,
+                        const int32_t* piv, hipStream_t stream) {
+  using S = GetrsShape<Real, N, NRHS, T>;
+  static_assert(S::BLOCK_BYTES == getrs_lds_bytes(N, T), "host and device LDS sizes disagree");
+  if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((getrs_kernel<Real, N, NRHS, T>), dim3((unsigned)p.grid),
+                     dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
+                     p.batch, static_cast<const Real*>(LU), piv, static_cast<const Real*>(B),
+                     static_cast<Real*>(X));
+  return (int)hipGetLastError();
+}
+
+template <typename Real, int N, int NRHS, int T>
+static int launch_op(const LaunchPlan& p, const void* in0, const void* in1, void* out,
+                     int32_t* piv, int32_t* info, hipStream_t stream) {
+  switch (p.op) {
+    case kOpGesv:
+      return launch_panel<Real, N, NRHS, T, false>(p, in0, in1, out, piv, info, stream);
+    case kOpGetrf:
+      if constexpr (NRHS == 1)
+        return launch_panel<Real, N, NRHS, T, true>(p, in0, nullptr, out, piv, info, stream);
+      else
+        return (int)hipErrorInvalidConfiguration;
+    case kOpGetrs:
+      return launch_getrs<Real, N, NRHS, T>(p, in0, in1, out, piv, stream);
+    default:
+      return (int)hipErrorInvalidConfiguration;
+  }
+}
+
 int TDLS_LAUNCHER_NAME(TDLS_INST_SFX, TDLS_INST_N, TDLS_INST_NRHS)(
-    const LaunchPlan& p, const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
-    hipStream_t stream) {
+    const LaunchPlan& p, const void* in0, const void* in1, void* out, int32_t* piv,
+    int32_t* info, hipStream_t stream) {
   using Real = TDLS_INST_REAL;
   constexpr int N = TDLS_INST_N;
   constexpr int NRHS = TDLS_INST_NRHS;
@@ -47,9 +79,9 @@ int TDLS_LAUNCHER_NAME(TDLS_INST_SFX, TDLS_INST_N, TDLS_INST_NRHS)(
   constexpr int T0 = pick_group_size(N, NRHS, is64);
   constexpr int T1 = alt_group_size(N, NRHS, is64);
   if (p.N != N || p.NRHS != NRHS) return (int)hipErrorInvalidConfiguration;
-  if (p.T == T0) return launch_instance<Real, N, NRHS, T0>(p, A, B, X, piv, info, stream);
+  if (p.T == T0) return launch_op<Real, N, NRHS, T0>(p, in0, in1, out, piv, info, stream);
   if constexpr (T1 != 0) {
-    if (p.T == T1) return launch_instance<Real, N, NRHS, T1>(p, A, B, X, piv, info, stream);
+    if (p.T == T1) return launch_op<Real, N, NRHS, T1>(p, in0, in1, out, piv, info, stream);
   }
   return (int)hipErrorInvalidConfiguration;
 }

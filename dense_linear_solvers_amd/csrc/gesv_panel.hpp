@@ -242,11 +242,15 @@ __device__ __forceinline__ uint32_t lo_word(double v) {
 
 // ------------------------------------------------------------- kernel
 
-template <typename Real, int N, int NRHS, int T, int B>
+// FACT = false: gesv, X receives the solutions.  FACT = true: getrf (NRHS
+// must be 1 and Bm is not read), X receives the factors in the layout of A:
+// LAPACK's row order, unit-lower L below the diagonal and U on and above it.
+template <typename Real, int N, int NRHS, int T, int B, bool FACT = false>
 __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     gesv_panel_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ A,
                       const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ piv,
                       int32_t* __restrict__ info) {
+  static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
   using S = PanelShape<Real, N, NRHS, T, B>;
   constexpr int R = S::R;
   constexpr int G = S::G;
@@ -309,7 +313,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           constexpr int j = decltype(jc)::value;
           sfor<0, R>([&](auto Kc) {
             constexpr int K = decltype(Kc)::value;
-            y[K][j] = br[K][COL ? j * N : j];
+            if constexpr (FACT)
+              y[K][j] = Real(0);
+            else
+              y[K][j] = br[K][COL ? j * N : j];
           });
         });
       };
@@ -341,7 +348,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         });
         sfor<0, NRHS>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
-          if (qrow && j < nrhs) y[K][j] = br[j * js];
+          if constexpr (!FACT)
+            if (qrow && j < nrhs) y[K][j] = br[j * js];
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -506,6 +514,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int K = decltype(Kc)::value;
         const Real l = a[K][k] / d;
         lm[i][K] = lab[K] > k ? l : Real(0);
+        if constexpr (FACT) {
+          a[K][k] = lab[K] > k ? l : a[K][k];   // L below the diagonal
+          asm volatile("" : "+v"(a[K][k]));       // settled now, not at the store
+        }
       });
       // (e) the rest of the panel takes this pivot's update now, so the next
       // column is complete when its search starts
@@ -586,6 +598,36 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       wave_sync_lds();  // records are rewritten by the next panel
     }
   });
+
+  if constexpr (FACT) {
+    // ---- factors: every row, whatever lane holds it, is row lab of L\U
+    // (multipliers before its position, U from it on); a failed system gets
+    // +0.0 everywhere and pivots -1.
+    const bool failed = status != 0;
+    if (live) {
+      Real* LUs = X + sys * ((int64_t)n * n);
+      int32_t* Ps = piv + sys * (int64_t)n;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = lab[K];
+        if (q >= 0 && q < n) {
+          // row q: one base address, column offsets (stride n in the
+          // column-major layout); a few stores at a time so that addresses
+          // are not all formed ahead of them
+          Real* rowp = LUs + (col ? (int64_t)q : (int64_t)q * n);
+          const int64_t cs = col ? n : 1;
+          sfor<0, N>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if (c < n) rowp[c * cs] = failed ? Real(0) : a[K][c];
+            if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+          });
+        }
+        const int qf = tx + K * T;
+        if (qf < n) Ps[qf] = failed ? -1 : pv[K];
+      });
+      if (tx == 0) info[sys] = status;
+    }
+  } else {
 
   // ---- back substitution.  Every row, whatever lane holds it, writes its
   // right-hand sides to the store at its position; the lanes read them back
@@ -760,6 +802,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     });
     if (tx == 0) info[sys] = status;
   }
+  }  // gesv
 }
 
 }  // namespace tdls

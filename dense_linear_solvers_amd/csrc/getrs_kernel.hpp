@@ -1,0 +1,210 @@
+// Batched getrs: X = A^-1 B from the factors that the factorization kernel
+// writes (P A = L U in LAPACK's row order, unit-lower L below the diagonal,
+// U on and above it, the 0-based swap sequence), one system per group of T
+// lanes of a wave64, lane tx holding the fixed positions tx, tx+T, ...
+//
+// What is computed (cited by page title and section):
+//  * "solver_static.hpp File Reference" (TDLS CooperativeLUpp), section
+//    Factored format: under physical interchanges the rows end in the
+//    pivoted order as in LAPACK, L's multipliers before the diagonal, U from
+//    it on, the pivots themselves on the diagonal, and the factorization is
+//    consumed by the substitution routines of the same solver; Detailed
+//    Description: the forward substitution L y = P b, then U x = y, the
+//    solution entry kept by the lane that owns its row.
+//  * "ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged
+//    numerical and failure contract: a failed factorization (every pivot
+//    -1) yields no usable solution, so its X is +0.0 everywhere; inputs are
+//    read only and results go to a separate buffer.
+//
+// Arithmetic order: the right-hand sides are gathered in the pivoted order
+// (the swaps applied in sequence), then y_r -= L(r,k) y_k for k = 0, 1, ...
+// and x_k = y_k / U(k,k), y_r -= U(r,k) x_k for k = n-1, ..., 0, each a
+// fused multiply-add; every element sees the operations of the elimination
+// that produced the factors in the same order, so factor-then-solve gives
+// the same bits as the one-call solve.
+#pragma once
+
+#include "gesv_panel.hpp"
+
+namespace tdls {
+
+template <typename Real, int N, int NRHS, int T>
+struct GetrsShape {
+  static_assert(T == 4 || T == 16 || T == 32 || T == 64, "group size must be 4, 16, 32 or 64");
+  static constexpr int R = (N + T - 1) / T;   // positions per lane
+  static constexpr int G = kWaveSize / T;     // systems per wave
+  static constexpr int SL = T < 16 ? T : 16;  // lanes per DPP broadcast domain
+  static constexpr int BLOCK_BYTES = kWavesPerBlock * G * N * (int)sizeof(int32_t);
+};
+
+template <typename Real, int N, int NRHS, int T>
+__global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
+    getrs_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ LU,
+                 const int32_t* __restrict__ piv, const Real* __restrict__ Bm,
+                 Real* __restrict__ X) {
+  using S = GetrsShape<Real, N, NRHS, T>;
+  constexpr int R = S::R;
+  constexpr int G = S::G;
+  constexpr int SL = S::SL;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x / kWaveSize;
+  const int g = lane / T;
+  const int tx = lane & (T - 1);
+  const int gbase = g * T;
+  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * G;
+  if (wave_first >= batch) return;  // the whole wave is past the batch
+  const int64_t sys = wave_first + g;
+  const bool live = sys < batch;
+  int32_t* pl = reinterpret_cast<int32_t*>(lds_raw) + (wave * G + g) * N;
+
+  // ---- the swap sequence to LDS (the identity past n and for groups past
+  // the batch), then the source row of each position: walking the swaps
+  // from the last to the first maps a position to the row it receives.
+  const int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    const int q = tx + K * T;
+    if (q < N) pl[q] = (live && q < n) ? Ps[q] : q;
+  });
+  wave_sync_lds();
+  const bool failed = pl[0] < 0;   // a failed factorization: every pivot -1
+  int src[R];
+  sfor<0, R>([&](auto Kc) { src[decltype(Kc)::value] = tx + decltype(Kc)::value * T; });
+  sfor<0, N>([&](auto ic) {
+    constexpr int k = N - 1 - decltype(ic)::value;
+    const int pk = failed ? k : pl[k];
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      src[K] = src[K] == k ? pk : (src[K] == pk ? k : src[K]);
+    });
+  });
+
+  // ---- load: row q of L\U and row src(q) of B for each position q of the
+  // lane; past n the factors are the identity and B is zero.  Source rows
+  // are clamped into the matrix, so a malformed pivot cannot address
+  // outside it.
+  Real a[R][N];
+  Real y[R][NRHS];
+  {
+    const Real* Ls = LU + (live ? sys : 0) * (int64_t)n * n;
+    const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      const bool qrow = live && q < n;
+      const int qq = qrow ? q : 0;
+      const int sr = src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]);
+      if (n == N && nrhs == NRHS) {
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          a[K][c] = Ls[col ? (int64_t)c * N + qq : (int64_t)qq * N + c];
+        });
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          y[K][j] = Bs[col ? (int64_t)j * N + sr : (int64_t)sr * NRHS + j];
+        });
+        if (q >= N) {
+          sfor<0, NRHS>([&](auto jc) { y[K][decltype(jc)::value] = Real(0); });
+        }
+      } else {
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          a[K][c] = (q == c) ? Real(1) : Real(0);
+          if (qrow && c < n) a[K][c] = Ls[col ? (int64_t)c * n + qq : (int64_t)qq * n + c];
+        });
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          y[K][j] = Real(0);
+          if (qrow && j < nrhs) y[K][j] = Bs[col ? (int64_t)j * n + sr : (int64_t)sr * nrhs + j];
+        });
+      }
+    });
+  }
+
+  // ---- L y = P b: y_k (lane k % T, slot k / T) leaves the rows below it.
+  // The slot of k itself goes last, so the broadcast source is not rewritten
+  // before the other slots have read it.
+  sfor<0, N - 1>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int kl = k % T;
+    constexpr int ks = k / T;
+    constexpr int SLK = kl % SL;
+    const Real mk = tx > kl ? a[ks][k] : Real(0);   // rows of slot ks below k
+    sfor<0, NRHS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (T <= 16) {
+        sfor<ks + 1, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          fnmac_bcast<T, SLK, K == ks + 1>(y[K][j], y[ks][j], a[K][k]);
+        });
+        fnmac_bcast<T, SLK, ks + 1 == R>(y[ks][j], y[ks][j], mk);
+      } else {
+        const Real yk = lane_fetch<T>(y[ks][j], gbase + kl);
+        sfor<ks + 1, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          y[K][j] = __builtin_fma(-a[K][k], yk, y[K][j]);
+        });
+        y[ks][j] = __builtin_fma(-mk, yk, y[ks][j]);
+      }
+    });
+  });
+
+  // ---- U x = y: x_k = y_k / U(k,k) on lane k % T, kept there, and removed
+  // from the rows above.
+  Real xr[R][NRHS];
+  sfor<0, R>([&](auto Kc) {
+    sfor<0, NRHS>([&](auto jc) { xr[decltype(Kc)::value][decltype(jc)::value] = Real(0); });
+  });
+  sfor<0, N>([&](auto ic) {
+    constexpr int k = N - 1 - decltype(ic)::value;
+    constexpr int kl = k % T;
+    constexpr int ks = k / T;
+    constexpr int SLK = kl % SL;
+    const Real mk = tx < kl ? a[ks][k] : Real(0);   // rows of slot ks above k
+    sfor<0, NRHS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const Real x = y[ks][j] / a[ks][k];   // meaningful on lane kl
+      xr[ks][j] = tx == kl ? x : xr[ks][j];
+      asm volatile("" : "+v"(xr[ks][j]));   // select now, not at the store
+      if constexpr (T <= 16) {
+        sfor<0, ks>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          fnmac_bcast<T, SLK, K == 0>(y[K][j], x, a[K][k]);
+        });
+        fnmac_bcast<T, SLK, ks == 0>(y[ks][j], x, mk);
+      } else {
+        const Real xk = lane_fetch<T>(x, gbase + kl);
+        sfor<0, ks>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          y[K][j] = __builtin_fma(-a[K][k], xk, y[K][j]);
+        });
+        y[ks][j] = __builtin_fma(-mk, xk, y[ks][j]);
+      }
+    });
+  });
+
+  // ---- store X (all +0.0 when the factorization failed)
+  if (live) {
+    Real* Xs = X + sys * ((int64_t)n * nrhs);
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      if (q < n) {
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if (j < nrhs) {
+            const Real v = failed ? Real(0) : xr[K][j];
+            if (col)
+              Xs[(int64_t)j * n + q] = v;
+            else
+              Xs[(int64_t)q * nrhs + j] = v;
+          }
+        });
+      }
+    });
+  }
+}
+
+}  // namespace tdls

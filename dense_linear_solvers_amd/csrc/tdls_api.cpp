@@ -33,6 +33,8 @@ struct ShapeEntry {
 const ShapeEntry kShapes[] = {TDLS_FOR_EACH_SHAPE(TDLS_SHAPE_ENTRY)};
 #undef TDLS_SHAPE_ENTRY
 
+int check_device();
+
 GesvLauncher find_launcher(int dtype, int N, int NRHS) {
   for (const ShapeEntry& e : kShapes)
     if (e.dtype == dtype && e.N == N && e.NRHS == NRHS) return e.launch;
@@ -55,7 +57,9 @@ int group_size_override() {
   return atoi(s);
 }
 
-int make_plan(int dtype, int layout, int n, int nrhs, int64_t batch, LaunchPlan* p) {
+// Scalar checks and launch plan of one operation.  The factorization runs
+// with one (unused) right-hand side, so `nrhs` is 1 for it.
+int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, LaunchPlan* p) {
   int rc = check_scalars(dtype, layout, n, nrhs, batch);
   if (rc != 0) return rc;
   const bool is64 = dtype == TDLS_F64;
@@ -64,6 +68,7 @@ int make_plan(int dtype, int layout, int n, int nrhs, int64_t batch, LaunchPlan*
     if (v >= n) { N = v; break; }
   for (int v : kNrhsValues)
     if (v >= nrhs) { NRHS = v; break; }
+  p->op = op;
   const int T0 = pick_group_size(N, NRHS, is64);
   const int T1 = alt_group_size(N, NRHS, is64);
   int T = T0;
@@ -86,8 +91,35 @@ int make_plan(int dtype, int layout, int n, int nrhs, int64_t batch, LaunchPlan*
   p->systems_per_block = (int64_t)kWavesPerBlock * p->G;
   p->grid = (batch + p->systems_per_block - 1) / p->systems_per_block;
   if (p->grid > 0x7fffffffLL) return -5;
-  p->lds_bytes = gesv_lds_bytes(N, NRHS, T, is64);
+  p->lds_bytes = op == kOpGetrs ? getrs_lds_bytes(N, T) : gesv_lds_bytes(N, NRHS, T, is64);
   return 0;
+}
+
+int fill_plan(const LaunchPlan& p, tdls_plan* out) {
+  if (out == nullptr) return -6;
+  out->n = p.n;
+  out->nrhs = p.nrhs;
+  out->n_kernel = p.N;
+  out->nrhs_kernel = p.NRHS;
+  out->group_size = p.T;
+  out->rows_per_lane = p.R;
+  out->systems_per_wave = p.G;
+  out->threads_per_block = p.threads_per_block;
+  out->systems_per_block = p.systems_per_block;
+  out->grid = p.grid;
+  out->lds_bytes = p.lds_bytes;
+  return 0;
+}
+
+int launch(const LaunchPlan& p, const void* in0, const void* in1, void* out, int32_t* piv,
+           int32_t* info, hipStream_t stream) {
+  int rc = check_device();
+  if (rc != 0) return rc;
+  GesvLauncher l = find_launcher(p.dtype, p.N, p.NRHS);
+  if (l == nullptr) return TDLS_ERR_NO_KERNEL;
+  const int err = l(p, in0, in1, out, piv, info, stream);
+  if (err == (int)hipErrorInvalidConfiguration) return TDLS_ERR_NO_KERNEL;
+  return err == 0 ? TDLS_SUCCESS : TDLS_ERR_LAUNCH;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -119,28 +151,27 @@ extern "C" {
 int tdls_plan_gesv(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                    tdls_plan* out) {
   tdls::LaunchPlan p;
-  int rc = tdls::make_plan((int)dtype, (int)layout, n, nrhs, batch, &p);
+  int rc = tdls::make_plan(tdls::kOpGesv, (int)dtype, (int)layout, n, nrhs, batch, &p);
   if (rc != 0) return rc;
-  if (out == nullptr) return -6;
-  out->n = p.n;
-  out->nrhs = p.nrhs;
-  out->n_kernel = p.N;
-  out->nrhs_kernel = p.NRHS;
-  out->group_size = p.T;
-  out->rows_per_lane = p.R;
-  out->systems_per_wave = p.G;
-  out->threads_per_block = p.threads_per_block;
-  out->systems_per_block = p.systems_per_block;
-  out->grid = p.grid;
-  out->lds_bytes = p.lds_bytes;
-  return 0;
+  return tdls::fill_plan(p, out);
+}
+
+int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nrhs,
+                 int64_t batch, tdls_plan* out) {
+  if (op != TDLS_OP_GESV && op != TDLS_OP_GETRF && op != TDLS_OP_GETRS) return -1;
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan((int)op, (int)dtype, (int)layout, n, op == TDLS_OP_GETRF ? 1 : nrhs,
+                           batch, &p);
+  if (rc != 0) return rc < 0 ? rc - 1 : rc;   // argument numbers shift by one
+  rc = tdls::fill_plan(p, out);
+  return rc == -6 ? -7 : rc;
 }
 
 int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                       const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
                       hipStream_t stream) {
   tdls::LaunchPlan p;
-  int rc = tdls::make_plan((int)dtype, (int)layout, n, nrhs, batch, &p);
+  int rc = tdls::make_plan(tdls::kOpGesv, (int)dtype, (int)layout, n, nrhs, batch, &p);
   if (rc != 0) return rc;
   if (batch == 0) return TDLS_SUCCESS;  // nothing to read or write, nothing launched
 
@@ -161,29 +192,68 @@ int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int
       tdls::overlaps(info, bytesI, B, bytesB) || tdls::overlaps(info, bytesI, X, bytesB) ||
       tdls::overlaps(info, bytesI, piv, bytesP))
     return -10;
+  return tdls::launch(p, A, B, X, piv, info, stream);
+}
 
-  rc = tdls::check_device();
+int tdls_getrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                       const void* A, void* LU, int32_t* piv, int32_t* info,
+                       hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpGetrf, (int)dtype, (int)layout, n, 1, batch, &p);
+  if (rc == -5) return -4;   // batch is argument 4 here
   if (rc != 0) return rc;
-  tdls::GesvLauncher launch = tdls::find_launcher(p.dtype, p.N, p.NRHS);
-  if (launch == nullptr) return TDLS_ERR_NO_KERNEL;
-  const int err = launch(p, A, B, X, piv, info, stream);
-  if (err == (int)hipErrorInvalidConfiguration) return TDLS_ERR_NO_KERNEL;
-  return err == 0 ? TDLS_SUCCESS : TDLS_ERR_LAUNCH;
+  if (batch == 0) return TDLS_SUCCESS;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesA = (size_t)batch * n * n * es;
+  const size_t bytesP = (size_t)batch * n * 4;
+  const size_t bytesI = (size_t)batch * 4;
+  if (A == nullptr || tdls::misaligned(A, es)) return -5;
+  if (LU == nullptr || tdls::misaligned(LU, es) || tdls::overlaps(LU, bytesA, A, bytesA))
+    return -6;
+  if (piv == nullptr || tdls::misaligned(piv, 4) || tdls::overlaps(piv, bytesP, A, bytesA) ||
+      tdls::overlaps(piv, bytesP, LU, bytesA))
+    return -7;
+  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
+      tdls::overlaps(info, bytesI, LU, bytesA) || tdls::overlaps(info, bytesI, piv, bytesP))
+    return -8;
+  return tdls::launch(p, A, nullptr, LU, piv, info, stream);
+}
+
+int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                       const void* LU, const int32_t* piv, const void* B, void* X,
+                       hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpGetrs, (int)dtype, (int)layout, n, nrhs, batch, &p);
+  if (rc != 0) return rc;
+  if (batch == 0) return TDLS_SUCCESS;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesLU = (size_t)batch * n * n * es;
+  const size_t bytesP = (size_t)batch * n * 4;
+  const size_t bytesB = (size_t)batch * n * nrhs * es;
+  if (LU == nullptr || tdls::misaligned(LU, es)) return -6;
+  if (piv == nullptr || tdls::misaligned(piv, 4)) return -7;
+  if (B == nullptr || tdls::misaligned(B, es)) return -8;
+  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, LU, bytesLU) ||
+      tdls::overlaps(X, bytesB, piv, bytesP) || tdls::overlaps(X, bytesB, B, bytesB))
+    return -9;
+  return tdls::launch(p, LU, B, X, const_cast<int32_t*>(piv), nullptr, stream);
 }
 
 const char* tdls_strerror(int code) {
   switch (code) {
     case TDLS_SUCCESS: return "success";
-    case -1: return "argument 1 (dtype) is invalid";
-    case -2: return "argument 2 (layout) is invalid";
-    case -3: return "argument 3 (n) is outside 1..64";
-    case -4: return "argument 4 (nrhs) is outside 1..8";
-    case -5: return "argument 5 (batch) is negative or too large";
-    case -6: return "argument 6 (A) is null or misaligned";
-    case -7: return "argument 7 (B) is null or misaligned";
-    case -8: return "argument 8 (X) is null, misaligned or overlaps an input";
-    case -9: return "argument 9 (piv) is null, misaligned or overlaps another buffer";
-    case -10: return "argument 10 (info) is null, misaligned or overlaps another buffer";
+    case -1: return "argument 1 is invalid (dtype, or op for tdls_plan_op)";
+    case -2: return "argument 2 is invalid (layout, or dtype for tdls_plan_op)";
+    case -3: return "argument 3 is invalid (n outside 1..64, or layout for tdls_plan_op)";
+    case -4: return "argument 4 is invalid (nrhs outside 1..8; batch for getrf; n for plan_op)";
+    case -5: return "argument 5 is invalid (batch; A for getrf; nrhs for plan_op)";
+    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; batch for plan_op)";
+    case -7: return "argument 7 is invalid (null, misaligned or overlapping buffer)";
+    case -8: return "argument 8 is invalid (null, misaligned or overlapping buffer)";
+    case -9: return "argument 9 is invalid (null, misaligned or overlapping buffer)";
+    case -10: return "argument 10 is invalid (null, misaligned or overlapping buffer)";
     case TDLS_ERR_LAUNCH: return "the kernel launch failed";
     case TDLS_ERR_DEVICE: return "the current device is not an MI355X (gfx950)";
     case TDLS_ERR_HIP: return "a HIP runtime query failed";

@@ -37,8 +37,12 @@ constexpr int kWaveSize = 64;
 // float64 systems would need 81 KiB and leave one wave per SIMD).
 constexpr int kWavesPerBlock = 1;
 
+// Operations the library launches.
+enum OpKind : int { kOpGesv = 0, kOpGetrf = 1, kOpGetrs = 2 };
+
 // Everything a launch needs, decided on the host before any launch.
 struct LaunchPlan {
+  int op;             // OpKind
   int dtype;          // 0 f32, 1 f64
   int layout;         // 0 row-major, 1 column-major
   int n, nrhs;        // problem
@@ -99,15 +103,22 @@ constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
   return kWavesPerBlock * (kWaveSize / T) * group * es;
 }
 
+// LDS bytes of one block (one wave) of the getrs kernel: the swap sequence
+// of each group.
+constexpr int getrs_lds_bytes(int N, int T) { return kWavesPerBlock * (kWaveSize / T) * N * 4; }
+
 // Launchers, one per shape of TDLS_FOR_EACH_SHAPE, defined in the
-// instantiation translation units.  They enqueue the kernel of p.T and
-// return a hipError_t value cast to int.
-using GesvLauncher = int (*)(const LaunchPlan& p, const void* A, const void* B, void* X,
+// instantiation translation units.  They enqueue the kernel of p.op and p.T
+// and return a hipError_t value cast to int.  Operands by op:
+//   gesv:  in0 = A, in1 = B, out = X, piv and info written;
+//   getrf: in0 = A, out = LU, piv and info written (NRHS = 1 shapes only);
+//   getrs: in0 = LU, in1 = B, out = X, piv read, info unused.
+using GesvLauncher = int (*)(const LaunchPlan& p, const void* in0, const void* in1, void* out,
                              int32_t* piv, int32_t* info, hipStream_t stream);
 #define TDLS_DECLARE_LAUNCHER(sfx, Real, N, NRHS)                                              \
-  int launch_gesv_##sfx##_n##N##_r##NRHS(const LaunchPlan& p, const void* A, const void* B,  \
-                                         void* X, int32_t* piv, int32_t* info,                \
-                                         hipStream_t stream);
+  int launch_gesv_##sfx##_n##N##_r##NRHS(const LaunchPlan& p, const void* in0,                \
+                                         const void* in1, void* out, int32_t* piv,            \
+                                         int32_t* info, hipStream_t stream);
 TDLS_FOR_EACH_SHAPE(TDLS_DECLARE_LAUNCHER)
 #undef TDLS_DECLARE_LAUNCHER
 

@@ -50,9 +50,16 @@ typedef enum tdls_layout {
   TDLS_COL_MAJOR = 1  /* A(r,c) at c*n + r;  B(r,j), X(r,j) at j*n + r    */
 } tdls_layout;
 
+/* Operations, for tdls_plan_op. */
+typedef enum tdls_op {
+  TDLS_OP_GESV = 0,  /* factor and solve in one call (tdls_gesv_batched) */
+  TDLS_OP_GETRF = 1, /* factor only (tdls_getrf_batched) */
+  TDLS_OP_GETRS = 2  /* solve from factors (tdls_getrs_batched) */
+} tdls_op;
+
 /* Return codes of the calls (not the per-system status, see `info`). */
 #define TDLS_SUCCESS 0
-/* -1 .. -10: the i-th argument of tdls_gesv_batched is invalid (LAPACK style). */
+/* -i: the i-th argument of the call is invalid (LAPACK style, 1-based). */
 #define TDLS_ERR_LAUNCH (-100)      /* the HIP launch failed (see tdls_strerror) */
 #define TDLS_ERR_DEVICE (-101)      /* the current device is not gfx950 */
 #define TDLS_ERR_HIP (-102)         /* a HIP query failed */
@@ -130,6 +137,75 @@ int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int
  */
 int tdls_plan_gesv(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                    tdls_plan* out);
+
+/*
+ * Factor A_s = P_s L_s U_s for s = 0 .. batch-1 on `stream` (LAPACK's
+ * getrf, the factorization half of tdls_gesv_batched).
+ *
+ * The elimination, pivot rule, tie rule, quotients and status are exactly
+ * those of tdls_gesv_batched ("solver_static.hpp File Reference", Detailed
+ * Description; "ruSOLVER：小矩阵 kernel 优化（实验性）", section on the
+ * unchanged numerical and failure contract).  The factors are written in the
+ * format of the TDLS page's section Factored format under physical
+ * interchanges, which is LAPACK's: row k of LU (in the layout of A) holds
+ * the multipliers of L before column k (unit diagonal implied) and the row
+ * of U from column k on, the pivot itself on the diagonal.
+ *
+ * Arguments (-i on rejection):
+ *   [1] dtype, [2] layout, [3] n (1..64): as for tdls_gesv_batched.
+ *   [4] batch   >= 0; 0 launches nothing.
+ *   [5] A       device, batch * n * n elements; read only.
+ *   [6] LU      device, batch * n * n elements, layout of A; written; must
+ *               not overlap A.
+ *   [7] piv     device, int32 [batch][n]; written: the 0-based swap
+ *               sequence (piv[s][k] >= k), or -1 everywhere for a failed
+ *               system.
+ *   [8] info    device, int32 [batch]; written: 0, or the 1-based step of
+ *               the first exactly zero pivot.  A failed system gets LU =
+ *               +0.0 and piv = -1 in every entry (its factors are not
+ *               usable, per the ruSOLVER contract).
+ *       stream  HIP stream.
+ * Ownership, stream semantics and errors as for tdls_gesv_batched.
+ */
+int tdls_getrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                       const void* A, void* LU, int32_t* piv, int32_t* info,
+                       hipStream_t stream);
+
+/*
+ * Solve A_s X_s = B_s from factors written by tdls_getrf_batched (LAPACK's
+ * getrs): the rows of B are taken in the pivoted order given by the swap
+ * sequence, then L y = P b (unit lower) and U x = y, the solution entry
+ * x_k = y_k / U(k,k) by IEEE division ("solver_static.hpp File Reference",
+ * sections Detailed Description and Factored format).  With the same
+ * layout, tdls_getrs_batched after tdls_getrf_batched yields the same bits
+ * as tdls_gesv_batched.
+ *
+ * Arguments (-i on rejection):
+ *   [1] dtype, [2] layout, [3] n (1..64), [4] nrhs (1..8), [5] batch: as for
+ *               tdls_gesv_batched.
+ *   [6] LU      device, batch * n * n elements; read only.
+ *   [7] piv     device, int32 [batch][n]; read only.  A system whose first
+ *               entry is negative (a failed factorization) gets X = +0.0.
+ *               Other entries outside 0..n-1 are clamped into the matrix
+ *               when the right-hand sides are gathered (no access outside
+ *               the system); the result is then unspecified.
+ *   [8] B       device, batch * n * nrhs elements; read only.
+ *   [9] X       device, like B; written; must not overlap LU, piv or B.
+ *       stream  HIP stream.
+ * A zero on the diagonal of U gives non-finite entries (no status here).
+ * Ownership, stream semantics and errors as for tdls_gesv_batched.
+ */
+int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                       const void* LU, const int32_t* piv, const void* B, void* X,
+                       hipStream_t stream);
+
+/*
+ * tdls_plan_gesv for any operation: [1] op, then the scalar arguments of
+ * tdls_plan_gesv shifted by one ([2] dtype ... [6] batch, [7] out); nrhs is
+ * ignored for TDLS_OP_GETRF.  Host only.
+ */
+int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nrhs,
+                 int64_t batch, tdls_plan* out);
 
 /* Static description of a return code (never NULL). */
 const char* tdls_strerror(int code);

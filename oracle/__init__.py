@@ -27,7 +27,7 @@ import numpy as np
 
 from .build import build, library_path
 
-__all__ = ["gesv", "getrf", "pivot_gap", "build", "library_path", "to_storage", "from_storage",
+__all__ = ["gesv", "getrf", "getrs", "pivot_gap", "build", "library_path", "to_storage", "from_storage",
            "rhs_to_storage", "rhs_from_storage", "max_threads", "use_library"]
 
 _LAYOUTS = {"row": 0, "col": 1}
@@ -49,6 +49,10 @@ def _load():
             g.restype = ctypes.c_int
             g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                           tp, tp, tp, i32p, i32p, ctypes.c_int]
+            r = getattr(lib, "oracle_getrs_" + sfx)
+            r.restype = ctypes.c_int
+            r.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                          tp, i32p, tp, tp, ctypes.c_int]
             f = getattr(lib, "oracle_getrf_" + sfx)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, tp, tp, i32p, i32p,
@@ -181,6 +185,31 @@ def getrf(A_store: np.ndarray, n: int, layout: str = "row", nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"oracle_getrf_{sfx} returned {rc}")
     return LU, ipiv, info, gap
+
+
+def getrs(LU_store: np.ndarray, ipiv: np.ndarray, B_store: np.ndarray, n: int, nrhs: int,
+          layout: str = "row", nthreads: int = 0) -> np.ndarray:
+    """Solve from factors: ``LU_store`` is the storage (in ``layout``) of the
+    factors in LAPACK's row order (see ``getrf``; convert its logical output
+    with ``to_storage``), ``ipiv`` int32 [batch, n] the 0-based swap sequence
+    (a system whose first entry is negative gets X = +0.0), ``B_store`` the
+    right-hand sides.  Returns X in B's storage."""
+    sfx, ct = _sfx(LU_store.dtype)
+    if np.dtype(B_store.dtype) != np.dtype(LU_store.dtype):
+        raise TypeError("LU and B must share a dtype")
+    LU = np.ascontiguousarray(LU_store).reshape(-1)
+    B = np.ascontiguousarray(B_store).reshape(-1)
+    P = np.ascontiguousarray(ipiv, dtype=np.int32).reshape(-1)
+    batch = LU.size // (n * n)
+    if LU.size != batch * n * n or B.size != batch * n * nrhs or P.size != batch * n:
+        raise ValueError("LU, ipiv and B sizes do not agree")
+    X = np.empty_like(B)
+    rc = getattr(_load(), "oracle_getrs_" + sfx)(
+        _LAYOUTS[layout], n, nrhs, batch, _ptr(LU, ct), _ptr(P, ctypes.c_int32), _ptr(B, ct),
+        _ptr(X, ct), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_getrs_{sfx} returned {rc}")
+    return X.reshape(np.shape(B_store))
 
 
 def pivot_gap(A_store: np.ndarray, n: int, layout: str = "row", nthreads: int = 0) -> np.ndarray:

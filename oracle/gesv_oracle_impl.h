@@ -196,6 +196,88 @@ static int SFX(getrf_one)(int layout, int n, const REAL *a, REAL *lu, int32_t *i
     return info;
 }
 
+/*
+ * getrs of one system: solve A x = b from the factors getrf writes (LAPACK's
+ * row order: L's multipliers strictly below the diagonal, unit diagonal
+ * implied, U on and above it), in the storage layout of the call.  The
+ * right-hand sides take the swaps of the sequence one after the other,
+ * then L y = P b is solved column by column (y_k leaves the rows below it),
+ * then U x = y exactly as in gesv_one.  This is the factor-then-solve split
+ * of the same elimination ("solver_static.hpp File Reference", Factored
+ * format and Detailed Description), so every entry sees the same fused
+ * multiply-adds in the same order as in gesv_one.  A failed factorization
+ * (ipiv[0] < 0, every pivot -1 by the ruSOLVER contract) gives x = +0.0.
+ */
+static void SFX(getrs_one)(int layout, int n, int nrhs, const REAL *lu, const int32_t *ipiv,
+                           const REAL *b, REAL *x, REAL *Y)
+{
+    if (ipiv[0] < 0) {
+        for (int r = 0; r < n; ++r)
+            for (int j = 0; j < nrhs; ++j)
+                x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;
+        return;
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)r * nrhs + j] = b[SFX(rhs_index)(layout, n, nrhs, r, j)];
+    for (int k = 0; k < n; ++k)
+        if (ipiv[k] != k)
+            SFX(swap_rows)(Y, nrhs, k, ipiv[k]);
+    for (int k = 0; k < n; ++k)
+        for (int r = k + 1; r < n; ++r) {
+            const REAL l = SFX(load_a)(lu, layout, n, r, k);
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)r * nrhs + j] = FMA(-l, Y[(size_t)k * nrhs + j], Y[(size_t)r * nrhs + j]);
+        }
+    for (int k = n - 1; k >= 0; --k) {
+        const REAL ukk = SFX(load_a)(lu, layout, n, k, k);
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / ukk;
+        for (int r = 0; r < k; ++r) {
+            const REAL u = SFX(load_a)(lu, layout, n, r, k);
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)r * nrhs + j] = FMA(-u, Y[(size_t)k * nrhs + j], Y[(size_t)r * nrhs + j]);
+        }
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            x[SFX(rhs_index)(layout, n, nrhs, r, j)] = Y[(size_t)r * nrhs + j];
+}
+
+int SFX(oracle_getrs)(int layout, int n, int nrhs, int64_t batch, const REAL *LU,
+                      const int32_t *ipiv, const REAL *B, REAL *X, int nthreads)
+{
+    int rc = oracle_check_args(layout, n, nrhs, batch);
+    if (rc != 0)
+        return rc;
+    if (batch == 0)
+        return 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+    for (int64_t s = 0; s < batch; ++s)
+        for (int k = 0; k < n; ++k) {
+            const int32_t p = ipiv[s * (int64_t)n + k];
+            if (ipiv[s * (int64_t)n] >= 0 && (p < k || p >= n))
+                return ORACLE_EINVAL; /* not a swap sequence */
+        }
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        REAL *Y = (REAL *)malloc(sizeof(REAL) * (size_t)n * nrhs);
+        if (Y == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t s = 0; s < batch; ++s)
+                SFX(getrs_one)(layout, n, nrhs, LU + s * (int64_t)n * n, ipiv + s * (int64_t)n,
+                               B + s * (int64_t)n * nrhs, X + s * (int64_t)n * nrhs, Y);
+        }
+        free(Y);
+    }
+    return failed ? ORACLE_ENOMEM : 0;
+}
+
 int SFX(oracle_gesv)(int layout, int n, int nrhs, int64_t batch, const REAL *A, const REAL *B,
                      REAL *X, int32_t *piv, int32_t *info, int nthreads)
 {

@@ -124,3 +124,73 @@ def test_group_size_override(lib, monkeypatch):
     monkeypatch.setenv("TDLS_GROUP_SIZE", "3")
     rc, _ = tdls.tdls_plan_gesv(tdls.F64, tdls.COL_MAJOR, 32, 1, 100)
     assert rc == -103
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 0, 8, 1), -1),
+    ((0, 5, 8, 1), -2),
+    ((0, 0, 0, 1), -3),
+    ((0, 0, 65, 1), -3),
+    ((0, 0, 8, -1), -4),
+])
+def test_getrf_scalar_validation(lib, args, code):
+    assert tdls.tdls_getrf_batched(*args, 0, 0, 0, 0, 0) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 0, 8, 1, 1), -1),
+    ((0, 5, 8, 1, 1), -2),
+    ((0, 0, 0, 1, 1), -3),
+    ((0, 0, 8, 0, 1), -4),
+    ((0, 0, 8, 9, 1), -4),
+    ((0, 0, 8, 1, -1), -5),
+])
+def test_getrs_scalar_validation(lib, args, code):
+    assert tdls.tdls_getrs_batched(*args, 0, 0, 0, 0, 0) == code
+
+
+def test_plan_op_validation_and_shapes(lib):
+    assert tdls.tdls_plan_op(9, 0, 0, 8, 1, 1)[0] == -1
+    assert tdls.tdls_plan_op(tdls.OP_GETRS, 7, 0, 8, 1, 1)[0] == -2
+    assert tdls.tdls_plan_op(tdls.OP_GETRS, 0, 0, 8, 9, 1)[0] == -5
+    assert tdls.tdls_plan_op(tdls.OP_GETRF, 0, 0, 8, 99, 1)[0] == 0   # nrhs ignored
+    assert tdls.tdls_plan_op(tdls.OP_GETRF, 0, 0, 8, 1, -1)[0] == -6
+    assert lib.tdls_plan_op(0, 0, 0, 8, 1, 1, None) == -7
+    for dtype in ("f32", "f64"):
+        for n in (1, 8, 13, 32, 64):
+            g = tdls.plan_gesv(dtype, "row", n, 1, 1000)
+            f = tdls.plan_op("getrf", dtype, "row", n, 1, 1000)
+            assert f["group_size"] == g["group_size"] and f["lds_bytes"] == g["lds_bytes"]
+            for nrhs in (1, 3, 8):
+                s = tdls.plan_op("getrs", dtype, "col", n, nrhs, 1000)
+                assert s["lds_bytes"] == s["systems_per_wave"] * s["n_kernel"] * 4
+                assert s["systems_per_block"] * s["grid"] >= 1000
+
+
+def test_factor_solve_pointer_validation(lib):
+    n, nrhs, batch = 16, 2, 10
+    es = 8
+    a = 1 << 40                                  # never dereferenced: every call fails
+    lu = a + batch * n * n * es                  # before the device is queried
+    pv = lu + batch * n * n * es
+    inf = pv + batch * n * 4
+    b = inf + batch * 4 + 64
+    x = b + batch * n * nrhs * es
+    f = lambda *p: tdls.tdls_getrf_batched(tdls.F64, tdls.COL_MAJOR, n, batch, *p, 0)
+    assert f(0, lu, pv, inf) == -5
+    assert f(a, 0, pv, inf) == -6
+    assert f(a, a + 8, pv, inf) == -6            # LU overlaps A
+    assert f(a, lu, 0, inf) == -7
+    assert f(a, lu, lu + 8, inf) == -7           # piv overlaps LU
+    assert f(a, lu, pv, 0) == -8
+    assert f(a, lu, pv, pv + 4) == -8            # info overlaps piv
+    s = lambda *p: tdls.tdls_getrs_batched(tdls.F64, tdls.COL_MAJOR, n, nrhs, batch, *p, 0)
+    assert s(0, pv, b, x) == -6
+    assert s(lu, 0, b, x) == -7
+    assert s(lu, pv + 2, b, x) == -7             # misaligned int32
+    assert s(lu, pv, 0, x) == -8
+    assert s(lu, pv, b, 0) == -9
+    assert s(lu, pv, b, b) == -9                 # X aliases B
+    assert s(lu, pv, b, lu) == -9                # X overlaps LU
+    assert tdls.tdls_getrf_batched(tdls.F64, tdls.ROW_MAJOR, n, 0, 0, 0, 0, 0, 0) == 0
+    assert tdls.tdls_getrs_batched(tdls.F64, tdls.ROW_MAJOR, n, 1, 0, 0, 0, 0, 0, 0) == 0

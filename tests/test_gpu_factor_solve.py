@@ -1,0 +1,272 @@
+"""GPU parity of the factor / solve split: getrf and getrs through the C
+interface vs the CPU oracle, and factor-then-solve vs the one-call solve.
+
+Bar (same as the one-call solve): info bit-exact; piv bit-exact on systems
+whose oracle pivot gap clears the margin, and -1 everywhere for a failed
+system; factors within the normwise tolerance of the working precision
+(1e-11 float64, 1e-4 float32; measured per system as max |LU - LU_oracle| /
+max |LU_oracle|) and all +0.0 for a failed system; solutions within the
+normwise tolerance on kappa <= 1e3 systems and the scaled residual <= 10.
+Factor-then-solve on the GPU must give the bits of the GPU's one-call
+solve, since both apply the same operations in the same order.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import golden_io
+import metrics
+import oracle
+import parity
+import dense_linear_solvers_amd as tdls
+from dense_linear_solvers_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np(dt):
+    return np.float32 if dt == "f32" else np.float64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tdls.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_getrf(A_st, layout):
+    A = torch.from_numpy(np.ascontiguousarray(A_st)).to(DEV)
+    LU, piv, info = tdls.getrf_batched(A, layout)
+    torch.cuda.synchronize()
+    return LU.cpu().numpy(), piv.cpu().numpy(), info.cpu().numpy()
+
+
+def gpu_getrs(LU_st, piv, B_st, layout):
+    LU = torch.from_numpy(np.ascontiguousarray(LU_st)).to(DEV)
+    P = torch.from_numpy(np.ascontiguousarray(piv, dtype=np.int32)).to(DEV)
+    B = torch.from_numpy(np.ascontiguousarray(B_st)).to(DEV)
+    X = tdls.getrs_batched(LU, P, B, layout)
+    torch.cuda.synchronize()
+    return X.cpu().numpy()
+
+
+def gpu_gesv(A_st, B_st, layout):
+    A = torch.from_numpy(np.ascontiguousarray(A_st)).to(DEV)
+    B = torch.from_numpy(np.ascontiguousarray(B_st)).to(DEV)
+    X, piv, info = tdls.gesv_batched(A, B, layout)
+    torch.cuda.synchronize()
+    return X.cpu().numpy(), piv.cpu().numpy(), info.cpu().numpy()
+
+
+def check_factors(A_st, n, layout, LU_st, piv, info, idx=None, what=""):
+    """Compare GPU factors with the oracle's on the systems ``idx``."""
+    dt = np.dtype(A_st.dtype)
+    A_st = A_st.reshape(-1, n * n)
+    batch = A_st.shape[0]
+    idx = np.arange(batch) if idx is None else np.asarray(idx)
+    LUo, ipo, info_o, gap = oracle.getrf(A_st[idx], n, layout)
+    LUg = oracle.from_storage(LU_st.reshape(-1, n * n)[idx], layout, n)
+    assert (info[idx] == info_o).all(), f"{what}: info mismatch"
+    ok = info_o == 0
+    margin = ok & (gap >= parity.GAP_TOL[dt])
+    assert (piv[idx][margin] == ipo[margin]).all(), f"{what}: piv mismatch"
+    assert (piv[idx][~ok] == -1).all(), f"{what}: failed pivots not -1"
+    assert (LUg[~ok] == 0).all() and not np.signbit(LUg[~ok]).any(), f"{what}: failed LU"
+    if margin.any():
+        num = np.abs(LUg[margin].astype(np.float64) - LUo[margin]).max(axis=(1, 2))
+        den = np.abs(LUo[margin].astype(np.float64)).max(axis=(1, 2))
+        err = (num / den).max()
+        print(f"{what}: systems={len(idx)} margin={int(margin.sum())} lu_err={err:.3e}",
+              flush=True)
+        assert err <= parity.X_TOL[dt], what
+    return LUo, ipo, info_o
+
+
+# ------------------------------------------------------------ hand-worked
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("n", [3, 8, 32, 64])
+def test_golden_examples_factor_and_solve(dtype, layout, n):
+    for ex in golden_io.all_examples():
+        e = golden_io.embed_identity(ex, n) if n > 3 else ex
+        A = e["A"][None].astype(_np(dtype))
+        b = e["b"][None, :, None].astype(_np(dtype))
+        A_st = oracle.to_storage(A, layout)
+        LU, piv, info = gpu_getrf(A_st, layout)
+        assert info[0] == e["info"], e["name"]
+        if e["info"] == 0:
+            np.testing.assert_array_equal(piv[0], e["ipiv"], err_msg=e["name"])
+            LUo, _, _, _ = oracle.getrf(A_st, n, layout)
+            # dyadic examples: the factors are exact
+            np.testing.assert_array_equal(oracle.from_storage(LU, layout, n), LUo)
+        else:
+            assert (piv == -1).all() and (LU == 0).all()
+        X = gpu_getrs(LU, piv, oracle.rhs_to_storage(b, layout), layout)
+        X = oracle.rhs_from_storage(X, layout, n, 1)
+        np.testing.assert_array_equal(X[0, :, 0], e["x"].astype(_np(dtype)), err_msg=e["name"])
+
+
+# -------------------------------------------------------------- recipes
+
+
+RECIPE_NAMES = sorted(workloads.RECIPES)
+
+
+@pytest.mark.parametrize("name", RECIPE_NAMES)
+def test_recipe_factor_solve_small(name):
+    """Every recipe at a batch spanning many blocks with a ragged tail:
+    getrf vs the oracle's factors, getrs on the oracle's factors vs the
+    oracle's getrs, and getrf+getrs vs the one-call solve, bit for bit."""
+    r = workloads.RECIPES[name]
+    spb = tdls.plan_op("getrf", r.dtype, r.layout, r.n, 1, 1)["systems_per_block"]
+    batch = 29 * spb + 3
+    w = workloads.make(name, seed=0, batch=batch, gap_fn=oracle.pivot_gap)
+    LU, piv, info = gpu_getrf(w.A, w.layout)
+    LUo, ipo, info_o = check_factors(w.A, w.n, w.layout, LU, piv, info, what=name)
+
+    # getrs from the oracle's own factors (failed systems marked by -1)
+    ipo = np.where(info_o[:, None] != 0, -1, ipo).astype(np.int32)
+    LUo_st = oracle.to_storage(LUo, w.layout)
+    Xg = gpu_getrs(LUo_st, ipo, w.B, w.layout)
+    Xo = oracle.getrs(LUo_st, ipo, w.B, w.n, w.nrhs, w.layout)
+    Xg_l = oracle.rhs_from_storage(Xg, w.layout, w.n, w.nrhs)
+    Xo_l = oracle.rhs_from_storage(Xo, w.layout, w.n, w.nrhs)
+    A_l = oracle.from_storage(w.A, w.layout, w.n)
+    B_l = oracle.rhs_from_storage(w.B, w.layout, w.n, w.nrhs)
+    ok = info_o == 0
+    kap = metrics.kappa_inf(A_l[ok])
+    err = metrics.normwise_error(Xg_l[ok], Xo_l[ok])
+    good = kap <= parity.KAPPA_MAX
+    if good.any():
+        assert err[good].max() <= parity.X_TOL[np.dtype(w.A.dtype)], name
+    res = metrics.residual_ratio(A_l[ok], Xg_l[ok], B_l[ok], w.A.dtype)
+    assert res.max() <= parity.RESID_TOL, name
+    assert (Xg_l[~ok] == 0).all() and not np.signbit(Xg_l[~ok]).any()
+
+    # factor then solve on the GPU == one-call solve on the GPU
+    X2 = gpu_getrs(LU, piv, w.B, w.layout)
+    X1, piv1, info1 = gpu_gesv(w.A, w.B, w.layout)
+    assert np.array_equal(X1.view(np.uint8), X2.view(np.uint8)), name
+    np.testing.assert_array_equal(info1, info)
+    np.testing.assert_array_equal(piv1, piv)
+
+
+def test_factor_full_size_sampled():
+    """The headline workload at full batch: factors checked on a sample."""
+    w = workloads.make("n32_f64_col", seed=0, gap_fn=oracle.pivot_gap)
+    LU, piv, info = gpu_getrf(w.A, w.layout)
+    rng = np.random.default_rng(77)
+    idx = np.unique(np.concatenate([[0, w.batch - 1],
+                                    rng.choice(w.batch, size=2000, replace=False)]))
+    check_factors(w.A, w.n, w.layout, LU, piv, info, idx=idx, what="n32_f64_col full")
+    assert (info == 0).all()
+    X2 = gpu_getrs(LU, piv, w.B, w.layout)
+    X1, _, _ = gpu_gesv(w.A, w.B, w.layout)
+    assert np.array_equal(X1.view(np.uint8), X2.view(np.uint8))
+
+
+# ------------------------------------------------------------ every shape
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_every_n_factor_then_solve(dtype, layout):
+    """n = 1..64 (padded kernels included), random nrhs, singular systems
+    mixed in: factors vs the oracle and factor+solve == one-call solve."""
+    rng = np.random.default_rng(31)
+    for n in range(1, 65):
+        nrhs = int(rng.integers(1, 9))
+        batch = int(rng.integers(1, 40))
+        A = rng.standard_normal((batch, n, n)) + 0.5 * np.eye(n)
+        if n > 2 and batch > 3:
+            A[2, :, n - 1] = 0                   # singular at the last step
+        B = rng.standard_normal((batch, n, nrhs))
+        A_st = oracle.to_storage(A.astype(_np(dtype)), layout)
+        B_st = oracle.rhs_to_storage(B.astype(_np(dtype)), layout)
+        LU, piv, info = gpu_getrf(A_st, layout)
+        check_factors(A_st, n, layout, LU, piv, info, what=f"{dtype} {layout} n={n}")
+        X2 = gpu_getrs(LU, piv, B_st, layout)
+        X1, _, _ = gpu_gesv(A_st, B_st, layout)
+        assert np.array_equal(X1.view(np.uint8), X2.view(np.uint8)), (dtype, layout, n)
+
+
+# ------------------------------------------------------------ invariances
+
+
+def test_group_size_does_not_change_factors_or_solutions(monkeypatch):
+    rng = np.random.default_rng(43)
+    compared = 0
+    for dtype in ("f32", "f64"):
+        for n, nrhs in ((8, 1), (16, 4), (24, 2), (32, 1), (32, 8)):
+            code = tdls.F64 if dtype == "f64" else tdls.F32
+            sizes = []
+            for t in (4, 16, 32, 64):
+                monkeypatch.setenv("TDLS_GROUP_SIZE", str(t))
+                ok_f = tdls.tdls_plan_op(tdls.OP_GETRF, code, tdls.ROW_MAJOR, n, 1, 1)[0] == 0
+                ok_s = tdls.tdls_plan_op(tdls.OP_GETRS, code, tdls.ROW_MAJOR, n, nrhs, 1)[0] == 0
+                if ok_f and ok_s:
+                    sizes.append(t)
+            monkeypatch.delenv("TDLS_GROUP_SIZE")
+            if len(sizes) < 2:
+                continue
+            A = rng.standard_normal((203, n, n)).astype(_np(dtype))
+            B = rng.standard_normal((203, n, nrhs)).astype(_np(dtype))
+            A[5, 2] = A[5, 0]
+            out = []
+            for t in sizes:
+                monkeypatch.setenv("TDLS_GROUP_SIZE", str(t))
+                LU, piv, info = gpu_getrf(A, "row")
+                out.append((LU, piv, info, gpu_getrs(LU, piv, B, "row")))
+            monkeypatch.delenv("TDLS_GROUP_SIZE")
+            for t, o in zip(sizes[1:], out[1:]):
+                for u, v in zip(out[0], o):
+                    np.testing.assert_array_equal(u, v, err_msg=f"{dtype} n={n} T={t}")
+            compared += 1
+    assert compared > 0
+
+
+# --------------------------------------------------------------- contract
+
+
+def test_factor_solve_contract_and_errors():
+    rng = np.random.default_rng(4)
+    A = torch.from_numpy(rng.standard_normal((500, 24, 24))).to(DEV)
+    B = torch.from_numpy(rng.standard_normal((500, 24, 3))).to(DEV)
+    A0, B0 = A.clone(), B.clone()
+    LU = torch.full_like(A, float("nan"))
+    piv = torch.full((500, 24), -7, dtype=torch.int32, device=DEV)
+    info = torch.full((500,), -7, dtype=torch.int32, device=DEV)
+    tdls.getrf_batched(A, "row", out=(LU, piv, info))
+    P0, LU0 = piv.clone(), LU.clone()
+    X = torch.full_like(B, float("nan"))
+    tdls.getrs_batched(LU, piv, B, "row", out=X)
+    torch.cuda.synchronize()
+    assert torch.equal(A, A0) and torch.equal(B, B0)
+    assert torch.equal(LU, LU0) and torch.equal(piv, P0)
+    assert torch.isfinite(LU).all() and (piv >= 0).all() and (info == 0).all()
+    assert torch.isfinite(X).all()
+    # empty batches
+    E = torch.zeros((0, 8, 8), dtype=torch.float32, device=DEV)
+    LUe, pe, ie = tdls.getrf_batched(E, "row")
+    assert LUe.shape == (0, 8, 8) and pe.shape == (0, 8) and ie.shape == (0,)
+    Xe = tdls.getrs_batched(LUe, pe, torch.zeros((0, 8, 2), device=DEV), "row")
+    assert Xe.shape == (0, 8, 2)
+    # aliasing is rejected before any launch
+    s = torch.cuda.current_stream().cuda_stream
+    rc = tdls.tdls_getrf_batched(tdls.F64, tdls.ROW_MAJOR, 24, 500, A.data_ptr(), A.data_ptr(),
+                                 piv.data_ptr(), info.data_ptr(), s)
+    assert rc == -6
+    rc = tdls.tdls_getrs_batched(tdls.F64, tdls.ROW_MAJOR, 24, 3, 500, LU.data_ptr(),
+                                 piv.data_ptr(), B.data_ptr(), B.data_ptr(), s)
+    assert rc == -9
+    torch.cuda.synchronize()

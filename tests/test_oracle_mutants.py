@@ -43,6 +43,19 @@ MUTANTS = {
     "info_zero_based": ("info = k + 1;\n            break;", "info = k;\n            break;"),
     "failed_piv_kept": ("piv[r] = -1;", "(void)0;"),
     "lu_multiplier_not_stored": ("lu[(size_t)r * n + k] = l;\n", "(void)l;\n"),
+    "getrs_swaps_reversed": ("for (int k = 0; k < n; ++k)\n        if (ipiv[k] != k)",
+                             "for (int k = n - 1; k >= 0; --k)\n        if (ipiv[k] != k)"),
+    "getrs_lower_transposed": ("const REAL l = SFX(load_a)(lu, layout, n, r, k);",
+                               "const REAL l = SFX(load_a)(lu, layout, n, k, r);"),
+    "getrs_upper_transposed": ("const REAL u = SFX(load_a)(lu, layout, n, r, k);",
+                               "const REAL u = SFX(load_a)(lu, layout, n, k, r);"),
+    "getrs_unit_diagonal_divided": (
+        "    for (int k = 0; k < n; ++k)\n        for (int r = k + 1; r < n; ++r) {",
+        "    for (int k = 0; k < n; ++k)\n        for (int r = k + 1 + 0 * (int)(Y[(size_t)k * nrhs] "
+        "/= SFX(load_a)(lu, layout, n, k, k)); r < n; ++r) {"),
+    "getrs_failed_negative_zero": (
+        "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;\n        return;",
+        "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = -(REAL)0;\n        return;"),
 }
 
 
@@ -56,6 +69,9 @@ def _selection():
     yield lambda: pins.test_exact_singularity_constructions(np.float64, "row")
     yield lambda: pins.test_exact_singularity_constructions(np.float32, "col")
     yield lambda: pins.test_cramer_exact(np.float64, "col", 3)
+    yield lambda: pins.test_getrs_exact_integer_factors(np.float64, "row")
+    yield lambda: pins.test_getrs_exact_integer_factors(np.float32, "col")
+    yield lambda: pins.test_getrs_failed_factorization_gives_zero(np.float64)
 
 
 def _build_variant(tmp_path, name, mutation):

@@ -418,3 +418,100 @@ def test_threads_do_not_change_results():
 def test_empty_batch():
     X, piv, info = oracle.gesv(np.zeros((0,)), np.zeros((0,)), 8, 1, "row")
     assert X.size == 0 and piv.shape == (0, 8) and info.shape == (0,)
+
+
+# ------------------------------------------------------------- getrs (split)
+
+
+def _random_swaps(rng, n):
+    """A LAPACK swap sequence: piv[k] drawn from k..n-1."""
+    return np.array([rng.integers(k, n) for k in range(n)], dtype=np.int32)
+
+
+def _exact_factor_system(rng, n, nrhs):
+    """Integer factors with an exactly known solution.
+
+    L unit lower and U upper with small integer entries, U's diagonal in
+    {+-1, +-2, +-4}, a random swap sequence piv and an integer solution x;
+    b = P^-1 (L U x) formed in exact integer arithmetic.  Every value the
+    substitutions meet is then a dyadic rational of a few bits, so a correct
+    getrs returns x exactly in float32 and float64."""
+    L = np.tril(rng.integers(-2, 3, (n, n)), -1) + np.eye(n, dtype=np.int64)
+    U = np.triu(rng.integers(-2, 3, (n, n)), 1)
+    U += np.diag(rng.choice([-4, -2, -1, 1, 2, 4], n))
+    piv = _random_swaps(rng, n)
+    x = rng.integers(-3, 4, (n, nrhs))
+    c = L @ (U @ x)                      # = P b
+    b = c.copy()
+    for k in range(n - 1, -1, -1):       # undo the swaps, last first
+        b[[k, piv[k]]] = b[[piv[k], k]]
+    LU = np.tril(L, -1) + U
+    return LU, piv, b, x
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_getrs_exact_integer_factors(dtype, layout):
+    """Solving from hand-made factors gives the exact solution (pins the swap
+    order, the unit diagonal of L, and which triangle is read where)."""
+    rng = np.random.default_rng(11)
+    for n, nrhs in [(1, 1), (3, 2), (6, 1), (9, 4), (16, 3)]:
+        LU, piv, b, x = _exact_factor_system(rng, n, nrhs)
+        X = oracle.getrs(oracle.to_storage(LU[None].astype(dtype), layout), piv[None],
+                         oracle.rhs_to_storage(b[None].astype(dtype), layout), n, nrhs, layout)
+        Xl = oracle.rhs_from_storage(X, layout, n, nrhs)[0]
+        np.testing.assert_array_equal(Xl, x.astype(dtype), err_msg=f"n={n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_getrs_matches_lapack(dtype, layout):
+    """Against LAPACK's getrs (SciPy lu_solve) on LAPACK's own factors."""
+    rng = np.random.default_rng(12)
+    n, nrhs, batch = 12, 3, 40
+    A = rng.standard_normal((batch, n, n)) + 4 * np.eye(n)
+    B = rng.standard_normal((batch, n, nrhs))
+    A = A.astype(dtype)
+    B = B.astype(dtype)
+    tol = 50 * n * np.finfo(dtype).eps
+    for s in range(batch):
+        lu, piv = scipy.linalg.lu_factor(A[s])
+        ref = scipy.linalg.lu_solve((lu, piv), B[s])
+        X = oracle.getrs(oracle.to_storage(lu[None], layout), piv[None].astype(np.int32),
+                         oracle.rhs_to_storage(B[s][None], layout), n, nrhs, layout)
+        Xl = oracle.rhs_from_storage(X, layout, n, nrhs)[0]
+        err = np.abs(Xl - ref).max() / np.abs(ref).max()
+        assert err <= tol, (s, err)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_getrs_failed_factorization_gives_zero(dtype):
+    n, nrhs = 5, 2
+    LU = np.ones((2, n, n), dtype=dtype)
+    piv = np.full((2, n), -1, dtype=np.int32)
+    piv[1] = np.arange(n)
+    LU[1] = np.eye(n, dtype=dtype)
+    B = np.full((2, n, nrhs), -3.0, dtype=dtype)
+    X = oracle.getrs(LU, piv, B, n, nrhs, "row")
+    assert (X[0] == 0).all() and not np.signbit(X[0]).any()
+    np.testing.assert_array_equal(X[1], B[1])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_factor_then_solve_is_gesv(dtype, layout):
+    """getrs after getrf repeats gesv's operations in gesv's order: the
+    same bits (singular systems included: both give +0.0)."""
+    rng = np.random.default_rng(13)
+    n, nrhs, batch = 10, 2, 60
+    A = rng.uniform(-1, 1, (batch, n, n)).astype(dtype)
+    A[::7, 4] = A[::7, 1]                       # some exactly singular systems
+    B = rng.uniform(-1, 1, (batch, n, nrhs)).astype(dtype)
+    As, Bs = oracle.to_storage(A, layout), oracle.rhs_to_storage(B, layout)
+    X, piv, info = oracle.gesv(As, Bs, n, nrhs, layout)
+    LU, ipiv, finfo, _ = oracle.getrf(As, n, layout)
+    np.testing.assert_array_equal(info, finfo)
+    ipiv = np.where(finfo[:, None] != 0, -1, ipiv).astype(np.int32)   # failed: pivots -1
+    X2 = oracle.getrs(oracle.to_storage(LU, layout), ipiv, Bs, n, nrhs, layout)
+    assert np.array_equal(X.view(np.uint8), X2.view(np.uint8))
+    assert (info[::7] != 0).all()
