@@ -13,7 +13,7 @@ object prices the kernel's algorithmic HBM bytes per launch against 8 TB/s;
 ``cpu_baseline`` is the plain CPU oracle timed on this host's cores on the
 same inputs.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--op gesv|getrf|getrs] [--no-cpu]
   python bench.py --calibrate-copy      # a plain 1 GiB device copy, for
                                         # scaling the HBM byte counters
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
@@ -37,19 +37,27 @@ METRIC = "systems/sec + achieved HBM GB/s, batched LUPP gesv n=32 fp32/fp64"
 DEFAULT_WORKLOAD = "n32_f64_col"
 
 
-def algorithmic_bytes(n: int, nrhs: int, es: int) -> int:
-    """Bytes the method must move per system: A read once, B read once, X,
-    piv and info written once."""
+def algorithmic_bytes(n: int, nrhs: int, es: int, op: str = "gesv") -> int:
+    """Bytes the method must move per system.  gesv: A and B read once, X,
+    piv and info written once.  getrf: A read once, LU, piv and info
+    written once.  getrs: LU, piv and B read once, X written once."""
+    if op == "getrf":
+        return 2 * n * n * es + 4 * n + 4
+    if op == "getrs":
+        return n * n * es + 4 * n + 2 * n * nrhs * es
     return n * n * es + 2 * n * nrhs * es + 4 * n + 4
 
 
-def algorithmic_flops(n: int, nrhs: int) -> int:
+def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
     """Per system: elimination 2*sum(m^2) multiply-add flops plus sum(m)
     divisions (m = n-1 .. 1), forward and back substitution on nrhs columns
-    2*n*(n-1) + n each."""
+    2*n*(n-1) + n each; getrf counts the elimination, getrs the
+    substitutions."""
     s2 = sum(m * m for m in range(1, n))
     s1 = sum(range(1, n))
-    return 2 * s2 + s1 + nrhs * (2 * n * (n - 1) + n)
+    elim = 2 * s2 + s1
+    subst = nrhs * (2 * n * (n - 1) + n)
+    return {"getrf": elim, "getrs": subst}.get(op, elim + subst)
 
 
 def kernel_source_hash() -> str:
@@ -130,7 +138,8 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
                       "reps": reps, "ms": dt * 1e3, "gbs": 2 * nbytes / dt / 1e9}), flush=True)
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
+def cpu_baseline(w, op: str = "gesv", min_seconds: float = 10.0,
+                 max_seconds: float = 30.0) -> dict:
     """The CPU oracle, as it stands, on all cores of this host, over the
     same inputs; repeated until at least ``min_seconds`` of work."""
     sys.path.insert(0, ROOT)
@@ -138,16 +147,29 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dic
     cores = len(os.sched_getaffinity(0))
     A = np.ascontiguousarray(w.A)
     B = np.ascontiguousarray(w.B)
+    n, nrhs, layout = w.n, w.nrhs, w.layout
+    if op == "getrs":
+        LU, ipiv, finfo, _ = oracle.getrf(A, n, layout, nthreads=cores)
+        LU = oracle.to_storage(LU, layout)
+        ipiv = np.where(finfo[:, None] != 0, -1, ipiv).astype(np.int32)
+
+    def run(cnt):
+        if op == "getrf":
+            oracle.getrf(A[:cnt], n, layout, nthreads=cores)
+        elif op == "getrs":
+            oracle.getrs(LU[:cnt], ipiv[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
+        else:
+            oracle.gesv(A[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
+
     # size one pass: the whole batch, or a prefix when a pass is too long
     t = time.perf_counter()
-    oracle.gesv(A[:2048], B[:2048], w.n, w.nrhs, w.layout, nthreads=cores)
+    run(2048)
     per_sys = max((time.perf_counter() - t) / 2048, 1e-9)
     count = int(min(w.batch, max(2048, max_seconds / 3 / per_sys)))
-    As, Bs = A[:count], B[:count]
     passes, solved = 0, 0
     t = time.perf_counter()
     while True:
-        oracle.gesv(As, Bs, w.n, w.nrhs, w.layout, nthreads=cores)
+        run(count)
         passes += 1
         solved += count
         el = time.perf_counter() - t
@@ -163,6 +185,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--op", default="gesv", choices=["gesv", "getrf", "getrs"],
+                    help="gesv (default: factor and solve in one call), getrf (factor only) "
+                         "or getrs (solve from factors made, untimed, by getrf)")
     ap.add_argument("--batch", type=int, default=0, help="override the recipe's batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -204,10 +229,20 @@ def main():
     info = torch.empty((w.batch,), dtype=torch.int32, device=dev)
     out = (X, piv, info)
     stream = torch.cuda.current_stream(dev)
-    plan = tdls.plan_gesv(w.dtype, w.layout, w.n, w.nrhs, w.batch)
+    op = args.op
+    plan = tdls.plan_op(op, w.dtype, w.layout, w.n, w.nrhs, w.batch)
+    if op == "gesv":
+        step = lambda: tdls.gesv_batched(A, B, w.layout, out=out)
+    elif op == "getrf":
+        LU = torch.empty_like(A)
+        step = lambda: tdls.getrf_batched(A, w.layout, out=(LU, piv, info))
+    else:
+        LU = torch.empty_like(A)
+        tdls.getrf_batched(A, w.layout, out=(LU, piv, info))     # factors, untimed
+        step = lambda: tdls.getrs_batched(LU, piv, B, w.layout, out=X)
 
     for _ in range(args.warmup):
-        tdls.gesv_batched(A, B, w.layout, out=out)
+        step()
     torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -216,14 +251,18 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        tdls.gesv_batched(A, B, w.layout, out=out)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
-    # sanity of the timed output (no oracle here): status and a residual sample
+    # sanity of the timed output (no oracle here): status and a residual
+    # sample (for getrf: the solve of the timed factors)
+    if op == "getrf":
+        tdls.getrs_batched(LU, piv, B, w.layout, out=X)
+        torch.cuda.synchronize()
     info_h = info.cpu().numpy()
     rng = np.random.default_rng(0)
     sample = torch.from_numpy(rng.choice(w.batch, size=min(w.batch, 512), replace=False)).to(dev)
@@ -239,8 +278,8 @@ def main():
     resid_max = float((res[ok] / den[ok]).max().item()) if bool(ok.any()) else 0.0
 
     es = 8 if w.dtype == "f64" else 4
-    bytes_per_launch = algorithmic_bytes(w.n, w.nrhs, es) * w.batch
-    flops_per_launch = algorithmic_flops(w.n, w.nrhs) * w.batch
+    bytes_per_launch = algorithmic_bytes(w.n, w.nrhs, es, op) * w.batch
+    flops_per_launch = algorithmic_flops(w.n, w.nrhs, op) * w.batch
     achieved_gbs = bytes_per_launch / (kernel_ms * 1e-3) / 1e9
     achieved_tflops = flops_per_launch / (kernel_ms * 1e-3) / 1e12
     vec_peak = FP64_VECTOR_PEAK_TFLOPS if w.dtype == "f64" else FP32_VECTOR_PEAK_TFLOPS
@@ -259,7 +298,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
+        "config": {"workload": w.name, "op": op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
                    "layout": "column-major" if w.layout == "col" else "row-major",
                    "distribution": w.meta.get("recipe"), "seed": 0,
                    **({"gap_filtered": False} if "gap_filtered" in w.meta else {}),
@@ -270,12 +309,12 @@ def main():
         "vector_frac": achieved_tflops / vec_peak,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name)},
+                     "traffic": measured_traffic(w.name) if op == "gesv" else None},
         "check": {"failed_systems": int((info_h != 0).sum()), "residual_max_sample": resid_max},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, op)
     print(json.dumps(result), flush=True)
 
 

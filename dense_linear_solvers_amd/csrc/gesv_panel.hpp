@@ -611,16 +611,32 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int K = decltype(Kc)::value;
         const int q = lab[K];
         if (q >= 0 && q < n) {
-          // row q: one base address, column offsets (stride n in the
-          // column-major layout); a few stores at a time so that addresses
-          // are not all formed ahead of them
-          Real* rowp = LUs + (col ? (int64_t)q : (int64_t)q * n);
-          const int64_t cs = col ? n : 1;
-          sfor<0, N>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            if (c < n) rowp[c * cs] = failed ? Real(0) : a[K][c];
-            if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
-          });
+          // row q: one base address and column offsets, compile-time ones
+          // for the kernel's own size (a row-major row is then one run of
+          // vector stores); a few stores at a time so that addresses are
+          // not all formed ahead of them
+          auto store_row = [&](auto colc, auto exactc) {
+            constexpr bool COL = decltype(colc)::value;
+            constexpr bool EXACT = decltype(exactc)::value;
+            const int64_t ld = EXACT ? N : n;
+            Real* rowp = LUs + (COL ? (int64_t)q : (int64_t)q * ld);
+            sfor<0, N>([&](auto cc) {
+              constexpr int c = decltype(cc)::value;
+              if (EXACT || c < n) rowp[COL ? c * ld : c] = failed ? Real(0) : a[K][c];
+              if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+            });
+          };
+          if (n == N) {
+            if (col)
+              store_row(std::true_type{}, std::true_type{});
+            else
+              store_row(std::false_type{}, std::true_type{});
+          } else {
+            if (col)
+              store_row(std::true_type{}, std::false_type{});
+            else
+              store_row(std::false_type{}, std::false_type{});
+          }
         }
         const int qf = tx + K * T;
         if (qf < n) Ps[qf] = failed ? -1 : pv[K];

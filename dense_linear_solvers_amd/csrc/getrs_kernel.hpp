@@ -97,17 +97,25 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       const int qq = qrow ? q : 0;
       const int sr = src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]);
       if (n == N && nrhs == NRHS) {
-        sfor<0, N>([&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-          a[K][c] = Ls[col ? (int64_t)c * N + qq : (int64_t)qq * N + c];
-        });
-        sfor<0, NRHS>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          y[K][j] = Bs[col ? (int64_t)j * N + sr : (int64_t)sr * NRHS + j];
-        });
-        if (q >= N) {
-          sfor<0, NRHS>([&](auto jc) { y[K][decltype(jc)::value] = Real(0); });
-        }
+        // the kernel's own size: compile-time offsets from one base per row
+        // (a row-major row is one run of vector loads)
+        auto load_exact = [&](auto colc) {
+          constexpr bool COL = decltype(colc)::value;
+          const Real* lr = Ls + (COL ? qq : qq * N);
+          const Real* br = Bs + (COL ? sr : sr * NRHS);
+          sfor<0, N>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            a[K][c] = lr[COL ? c * N : c];
+          });
+          sfor<0, NRHS>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            y[K][j] = q < N ? br[COL ? j * N : j] : Real(0);
+          });
+        };
+        if (col)
+          load_exact(std::true_type{});
+        else
+          load_exact(std::false_type{});
       } else {
         sfor<0, N>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
