@@ -27,7 +27,7 @@ import numpy as np
 
 from .build import build, library_path
 
-__all__ = ["gesv", "getrf", "getrs", "pivot_gap", "build", "library_path", "to_storage", "from_storage",
+__all__ = ["gesv", "getrf", "getrs", "potrf", "posv", "pivot_gap", "build", "library_path", "to_storage", "from_storage",
            "rhs_to_storage", "rhs_from_storage", "max_threads", "use_library"]
 
 _LAYOUTS = {"row": 0, "col": 1}
@@ -53,6 +53,14 @@ def _load():
             r.restype = ctypes.c_int
             r.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                           tp, i32p, tp, tp, ctypes.c_int]
+            c = getattr(lib, "oracle_potrf_" + sfx)
+            c.restype = ctypes.c_int
+            c.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_double, tp, tp,
+                          i32p, ctypes.c_int]
+            v = getattr(lib, "oracle_posv_" + sfx)
+            v.restype = ctypes.c_int
+            v.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                          ctypes.c_double, tp, tp, tp, i32p, ctypes.c_int]
             f = getattr(lib, "oracle_getrf_" + sfx)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, tp, tp, i32p, i32p,
@@ -210,6 +218,47 @@ def getrs(LU_store: np.ndarray, ipiv: np.ndarray, B_store: np.ndarray, n: int, n
     if rc != 0:
         raise RuntimeError(f"oracle_getrs_{sfx} returned {rc}")
     return X.reshape(np.shape(B_store))
+
+
+def potrf(A_store: np.ndarray, n: int, layout: str = "row", shift: float = 0.0,
+          nthreads: int = 0):
+    """Cholesky factors of A + shift I.  Returns ``(L, info)``: L float
+    [batch, n, n] logical row-major (lower triangular, zero above; all +0.0
+    for a failed system), info int32 [batch] (0; j+1 for the first
+    non-positive pivot; -2 for a matrix that is not exactly symmetric)."""
+    sfx, ct = _sfx(A_store.dtype)
+    A = np.ascontiguousarray(A_store).reshape(-1)
+    batch = A.size // (n * n)
+    if A.size != batch * n * n:
+        raise ValueError("A size is not a multiple of n*n")
+    L = np.empty((batch, n, n), dtype=A.dtype)
+    info = np.empty((batch,), dtype=np.int32)
+    rc = getattr(_load(), "oracle_potrf_" + sfx)(
+        _LAYOUTS[layout], n, batch, float(shift), _ptr(A, ct), _ptr(L, ct),
+        _ptr(info, ctypes.c_int32), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_potrf_{sfx} returned {rc}")
+    return L, info
+
+
+def posv(A_store: np.ndarray, B_store: np.ndarray, n: int, nrhs: int, layout: str = "row",
+         shift: float = 0.0, nthreads: int = 0):
+    """Solve (A + shift I) X = B by Cholesky.  Returns ``(X_store, info)``
+    with the status of ``potrf``; a failed system gets X = +0.0."""
+    sfx, ct = _sfx(A_store.dtype)
+    A = np.ascontiguousarray(A_store).reshape(-1)
+    B = np.ascontiguousarray(B_store).reshape(-1)
+    batch = A.size // (n * n)
+    if A.size != batch * n * n or B.size != batch * n * nrhs:
+        raise ValueError("A and B sizes do not agree")
+    X = np.empty_like(B)
+    info = np.empty((batch,), dtype=np.int32)
+    rc = getattr(_load(), "oracle_posv_" + sfx)(
+        _LAYOUTS[layout], n, nrhs, batch, float(shift), _ptr(A, ct), _ptr(B, ct), _ptr(X, ct),
+        _ptr(info, ctypes.c_int32), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_posv_{sfx} returned {rc}")
+    return X.reshape(np.shape(B_store)), info
 
 
 def pivot_gap(A_store: np.ndarray, n: int, layout: str = "row", nthreads: int = 0) -> np.ndarray:

@@ -28,6 +28,12 @@
  *  - piv[k] is the 0-based LAPACK swap sequence: the position exchanged with
  *    k at step k.
  *
+ * The same file holds the Cholesky factorization and solve of symmetric
+ * positive definite systems (potrf, posv) under the ruSOLVER contract for
+ * that path: exact symmetry check (status -2), explicit diagonal shift,
+ * inner products in increasing k, status j+1 for the first non-positive
+ * pivot, failed systems zeroed.
+ *
  * Not done here, on purpose: the whole-matrix max-abs scaling and the
  * non-finite status codes of the ruSOLVER contract (not part of this path).
  *
@@ -59,20 +65,24 @@ static int oracle_check_args(int layout, int n, int nrhs, int64_t batch)
 #define SFX(x) x##_f64
 #define FMA fma
 #define FABS fabs
+#define SQRT sqrt
 #include "gesv_oracle_impl.h"
 #undef REAL
 #undef SFX
 #undef FMA
 #undef FABS
+#undef SQRT
 
 #define REAL float
 #define SFX(x) x##_f32
 #define FMA fmaf
 #define FABS fabsf
+#define SQRT sqrtf
 #include "gesv_oracle_impl.h"
 #undef REAL
 #undef SFX
 #undef FMA
 #undef FABS
+#undef SQRT
 
 int oracle_max_threads(void) { return omp_get_max_threads(); }

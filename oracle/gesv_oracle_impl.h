@@ -12,6 +12,7 @@
  *   SFX(x) appends the suffix (_f64 / _f32) to an identifier
  *   FMA    fused multiply-add of REAL (fma / fmaf)
  *   FABS   absolute value of REAL (fabs / fabsf)
+ *   SQRT   square root of REAL, correctly rounded (sqrt / sqrtf)
  */
 
 /* Logical element (r, c) of the matrix of one system, whatever its storage.
@@ -273,6 +274,149 @@ int SFX(oracle_getrs)(int layout, int n, int nrhs, int64_t batch, const REAL *LU
                 SFX(getrs_one)(layout, n, nrhs, LU + s * (int64_t)n * n, ipiv + s * (int64_t)n,
                                B + s * (int64_t)n * nrhs, X + s * (int64_t)n * nrhs, Y);
         }
+        free(Y);
+    }
+    return failed ? ORACLE_ENOMEM : 0;
+}
+
+/*
+ * Cholesky of one system, A + shift I = L L^T, then (posv) L y = b and
+ * L^T x = y.  L is lower triangular, logical row-major n*n, zero above the
+ * diagonal.
+ *
+ * Contract ("ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged
+ * numerical and failure contract; "cuSolverDx potrf" function page):
+ *  - the input must be exactly symmetric, A(i,j) == A(j,i) in the working
+ *    precision, else status -2;
+ *  - the diagonal shift is explicit: s = A(j,j) + shift, rounded once, and
+ *    nothing else is added;
+ *  - inner products accumulate in increasing k: s = fma(-L(j,k), L(j,k), s)
+ *    for k = 0, 1, ..., j-1, then L(j,j) = sqrt(s) (IEEE square root), and
+ *    t = A(i,j), t = fma(-L(i,k), L(j,k), t) for k < j, L(i,j) = t / L(j,j)
+ *    (IEEE division) for i > j;
+ *  - status j+1 (1-based) for the first step whose s is not > 0 (the
+ *    smallest leading minor that is not positive definite, as cuSolverDx
+ *    reports it); a failed system (any nonzero status) gets L = +0.0 and
+ *    x = +0.0 everywhere.
+ * The lower triangle is read; the symmetry check makes the choice moot.
+ *
+ * The solves: y_i = b_i - sum_{k<i} L(i,k) y_k in increasing k, then
+ * y_i / L(i,i) (each y_k leaves the rows below it before the next one is
+ * formed), and x_j = y_j / L(j,j) for j = n-1 .. 0, each x_j then removed
+ * from the rows above it: y_i = fma(-L(j,i), x_j, y_i).
+ */
+static int SFX(potrf_one)(int layout, int n, REAL shift, const REAL *a, REAL *L)
+{
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < i; ++j)
+            if (!(SFX(load_a)(a, layout, n, i, j) == SFX(load_a)(a, layout, n, j, i)))
+                return -2;
+    for (size_t e = 0; e < (size_t)n * n; ++e)
+        L[e] = 0;
+    for (int j = 0; j < n; ++j) {
+        REAL s = SFX(load_a)(a, layout, n, j, j) + shift;
+        for (int k = 0; k < j; ++k)
+            s = FMA(-L[(size_t)j * n + k], L[(size_t)j * n + k], s);
+        if (!(s > 0))
+            return j + 1;
+        const REAL d = SQRT(s);
+        L[(size_t)j * n + j] = d;
+        for (int i = j + 1; i < n; ++i) {
+            REAL t = SFX(load_a)(a, layout, n, i, j);
+            for (int k = 0; k < j; ++k)
+                t = FMA(-L[(size_t)i * n + k], L[(size_t)j * n + k], t);
+            L[(size_t)i * n + j] = t / d;
+        }
+    }
+    return 0;
+}
+
+static int SFX(posv_one)(int layout, int n, int nrhs, REAL shift, const REAL *a, const REAL *b,
+                         REAL *x, REAL *L, REAL *Y)
+{
+    int info = SFX(potrf_one)(layout, n, shift, a, L);
+    if (info != 0) {
+        for (int r = 0; r < n; ++r)
+            for (int j = 0; j < nrhs; ++j)
+                x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;
+        return info;
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)r * nrhs + j] = b[SFX(rhs_index)(layout, n, nrhs, r, j)];
+    /* L y = b */
+    for (int k = 0; k < n; ++k) {
+        const REAL d = L[(size_t)k * n + k];
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / d;
+        for (int i = k + 1; i < n; ++i)
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)i * nrhs + j] =
+                    FMA(-L[(size_t)i * n + k], Y[(size_t)k * nrhs + j], Y[(size_t)i * nrhs + j]);
+    }
+    /* L^T x = y */
+    for (int k = n - 1; k >= 0; --k) {
+        const REAL d = L[(size_t)k * n + k];
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / d;
+        for (int i = 0; i < k; ++i)
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)i * nrhs + j] =
+                    FMA(-L[(size_t)k * n + i], Y[(size_t)k * nrhs + j], Y[(size_t)i * nrhs + j]);
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            x[SFX(rhs_index)(layout, n, nrhs, r, j)] = Y[(size_t)r * nrhs + j];
+    return 0;
+}
+
+int SFX(oracle_potrf)(int layout, int n, int64_t batch, double shift, const REAL *A, REAL *Lout,
+                      int32_t *info, int nthreads)
+{
+    int rc = oracle_check_args(layout, n, 1, batch);
+    if (rc != 0)
+        return rc;
+    if (batch == 0)
+        return 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t s = 0; s < batch; ++s) {
+        REAL *Ls = Lout + s * (int64_t)n * n;   /* logical row-major */
+        info[s] = SFX(potrf_one)(layout, n, (REAL)shift, A + s * (int64_t)n * n, Ls);
+        if (info[s] != 0)
+            for (size_t e = 0; e < (size_t)n * n; ++e)
+                Ls[e] = 0;
+    }
+    return 0;
+}
+
+int SFX(oracle_posv)(int layout, int n, int nrhs, int64_t batch, double shift, const REAL *A,
+                     const REAL *B, REAL *X, int32_t *info, int nthreads)
+{
+    int rc = oracle_check_args(layout, n, nrhs, batch);
+    if (rc != 0)
+        return rc;
+    if (batch == 0)
+        return 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        REAL *L = (REAL *)malloc(sizeof(REAL) * (size_t)n * n);
+        REAL *Y = (REAL *)malloc(sizeof(REAL) * (size_t)n * nrhs);
+        if (L == NULL || Y == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t s = 0; s < batch; ++s)
+                info[s] = SFX(posv_one)(layout, n, nrhs, (REAL)shift, A + s * (int64_t)n * n,
+                                        B + s * (int64_t)n * nrhs, X + s * (int64_t)n * nrhs, L,
+                                        Y);
+        }
+        free(L);
         free(Y);
     }
     return failed ? ORACLE_ENOMEM : 0;

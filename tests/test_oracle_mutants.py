@@ -53,6 +53,22 @@ MUTANTS = {
         "    for (int k = 0; k < n; ++k)\n        for (int r = k + 1; r < n; ++r) {",
         "    for (int k = 0; k < n; ++k)\n        for (int r = k + 1 + 0 * (int)(Y[(size_t)k * nrhs] "
         "/= SFX(load_a)(lu, layout, n, k, k)); r < n; ++r) {"),
+    "chol_diag_sign": ("s = FMA(-L[(size_t)j * n + k], L[(size_t)j * n + k], s);",
+                       "s = FMA(L[(size_t)j * n + k], L[(size_t)j * n + k], s);"),
+    "chol_offdiag_transposed": ("t = FMA(-L[(size_t)i * n + k], L[(size_t)j * n + k], t);",
+                                "t = FMA(-L[(size_t)k * n + i], L[(size_t)j * n + k], t);"),
+    "chol_no_sqrt": ("const REAL d = SQRT(s);", "const REAL d = s;"),
+    "chol_wrong_column": ("REAL t = SFX(load_a)(a, layout, n, i, j);",
+                          "REAL t = SFX(load_a)(a, layout, n, i, (j + 1) % n);"),
+    "chol_status_zero_based": ("if (!(s > 0))\n            return j + 1;",
+                               "if (!(s > 0))\n            return j;"),
+    "chol_no_symmetry_check": ("                return -2;", "                (void)0;"),
+    "chol_shift_ignored": ("REAL s = SFX(load_a)(a, layout, n, j, j) + shift;",
+                           "REAL s = SFX(load_a)(a, layout, n, j, j);"),
+    "chol_back_transposed": ("FMA(-L[(size_t)k * n + i], Y[(size_t)k * nrhs + j], "
+                             "Y[(size_t)i * nrhs + j]);\n    }\n    for (int r = 0;",
+                             "FMA(-L[(size_t)i * n + k], Y[(size_t)k * nrhs + j], "
+                             "Y[(size_t)i * nrhs + j]);\n    }\n    for (int r = 0;"),
     "getrs_failed_negative_zero": (
         "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;\n        return;",
         "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = -(REAL)0;\n        return;"),
@@ -72,6 +88,10 @@ def _selection():
     yield lambda: pins.test_getrs_exact_integer_factors(np.float64, "row")
     yield lambda: pins.test_getrs_exact_integer_factors(np.float32, "col")
     yield lambda: pins.test_getrs_failed_factorization_gives_zero(np.float64)
+    yield lambda: pins.test_cholesky_exact_integer_factors(np.float64, "row")
+    yield lambda: pins.test_cholesky_exact_integer_factors(np.float32, "col")
+    yield lambda: pins.test_cholesky_symmetry_and_shift(np.float64)
+    yield lambda: pins.test_cholesky_first_failing_minor()
 
 
 def _build_variant(tmp_path, name, mutation):

@@ -515,3 +515,104 @@ def test_factor_then_solve_is_gesv(dtype, layout):
     X2 = oracle.getrs(oracle.to_storage(LU, layout), ipiv, Bs, n, nrhs, layout)
     assert np.array_equal(X.view(np.uint8), X2.view(np.uint8))
     assert (info[::7] != 0).all()
+
+
+# ---------------------------------------------------------------- Cholesky
+
+
+def _exact_spd(rng, n, nrhs):
+    """L with small integer entries below the diagonal and a diagonal in
+    {1, 2, 4}, A = L L^T and b = A x for an integer x, all exact integers:
+    the factorization meets perfect squares and exact quotients only, so a
+    correct potrf returns L and a correct posv returns x, bit for bit."""
+    L = np.tril(rng.integers(-2, 3, (n, n)), -1) + np.diag(rng.choice([1, 2, 4], n))
+    A = L @ L.T
+    x = rng.integers(-3, 4, (n, nrhs))
+    return L, A, x, A @ x
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_cholesky_exact_integer_factors(dtype, layout):
+    rng = np.random.default_rng(21)
+    for n, nrhs in [(1, 1), (2, 3), (5, 1), (8, 2), (12, 4)]:
+        L, A, x, b = _exact_spd(rng, n, nrhs)
+        Lo, info = oracle.potrf(oracle.to_storage(A[None].astype(dtype), layout), n, layout)
+        assert info[0] == 0
+        np.testing.assert_array_equal(Lo[0], L.astype(dtype), err_msg=f"n={n}")
+        X, info = oracle.posv(oracle.to_storage(A[None].astype(dtype), layout),
+                              oracle.rhs_to_storage(b[None].astype(dtype), layout), n, nrhs,
+                              layout)
+        np.testing.assert_array_equal(oracle.rhs_from_storage(X, layout, n, nrhs)[0],
+                                      x.astype(dtype), err_msg=f"n={n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_cholesky_matches_lapack(dtype, layout):
+    """Against LAPACK's potrf/potrs (SciPy cho_factor / cho_solve)."""
+    rng = np.random.default_rng(22)
+    n, nrhs, batch = 16, 3, 30
+    M = rng.standard_normal((batch, n, n))
+    A = (M @ M.transpose(0, 2, 1) + n * np.eye(n)).astype(dtype)
+    A = (A + A.transpose(0, 2, 1)) / 2                   # exactly symmetric after rounding
+    B = rng.standard_normal((batch, n, nrhs)).astype(dtype)
+    L, info = oracle.potrf(oracle.to_storage(A, layout), n, layout)
+    X, xinfo = oracle.posv(oracle.to_storage(A, layout), oracle.rhs_to_storage(B, layout), n,
+                           nrhs, layout)
+    X = oracle.rhs_from_storage(X, layout, n, nrhs)
+    assert (info == 0).all() and (xinfo == 0).all()
+    tol = 50 * n * np.finfo(dtype).eps
+    for s in range(batch):
+        c, low = scipy.linalg.cho_factor(A[s], lower=True)
+        ref_L = np.tril(c)
+        assert np.abs(L[s] - ref_L).max() <= tol * np.abs(ref_L).max(), s
+        ref_x = scipy.linalg.cho_solve((c, low), B[s])
+        assert np.abs(X[s] - ref_x).max() <= tol * np.abs(ref_x).max() * 10, s
+
+
+def test_cholesky_first_failing_minor():
+    """Status j+1 for the smallest leading minor that is not positive
+    definite, pinned by the eigenvalues of the leading blocks."""
+    rng = np.random.default_rng(23)
+    n = 9
+    checked = 0
+    for _ in range(200):
+        Q = np.linalg.qr(rng.standard_normal((n, n)))[0]
+        ev = rng.uniform(0.5, 2.0, n)
+        ev[rng.integers(0, n)] = -rng.uniform(0.5, 2.0)       # indefinite
+        A = Q @ np.diag(ev) @ Q.T
+        A = (A + A.T) / 2
+        mins = [np.linalg.eigvalsh(A[:k, :k]).min() for k in range(1, n + 1)]
+        first = next(k for k, m in enumerate(mins, 1) if m <= 0)
+        if min(abs(m) for m in mins) < 1e-6:
+            continue                                          # too close to call
+        L, info = oracle.potrf(A[None], n, "row")
+        assert info[0] == first
+        assert (L == 0).all() and not np.signbit(L).any()
+        checked += 1
+    assert checked > 100
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_cholesky_symmetry_and_shift(dtype):
+    rng = np.random.default_rng(24)
+    n = 7
+    L0, A, x, b = _exact_spd(rng, n, 1)
+    A = A.astype(dtype)
+    # one off-diagonal pair differs by one unit in the last place: -2
+    Ab = A.copy()
+    Ab[5, 2] = np.nextafter(Ab[5, 2], dtype(np.inf))
+    L, info = oracle.potrf(np.stack([A, Ab]), n, "row")
+    assert list(info) == [0, -2]
+    X, xinfo = oracle.posv(np.stack([A, Ab]), np.stack([b, b]).astype(dtype), n, 1, "row")
+    assert list(xinfo) == [0, -2] and (X[1] == 0).all() and not np.signbit(X[1]).any()
+    # the shift is added to the diagonal once, nothing else: potrf(A, s) is
+    # potrf(A + s I) whenever A(j,j) + s is exact
+    s = 3.0
+    L1, _ = oracle.potrf(A[None], n, "row", shift=s)
+    L2, _ = oracle.potrf((A + s * np.eye(n, dtype=dtype))[None], n, "row")
+    np.testing.assert_array_equal(L1, L2)
+    # a shift that makes the first pivot non-positive fails at step 1
+    _, info = oracle.potrf(A[None], n, "row", shift=-float(A[0, 0]))
+    assert info[0] == 1
