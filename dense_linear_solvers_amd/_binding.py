@@ -39,9 +39,11 @@ class Plan(ctypes.Structure):
 
 
 EXPORTED = ("tdls_gesv_batched", "tdls_getrf_batched", "tdls_getrs_batched", "tdls_plan_gesv",
-            "tdls_plan_op", "tdls_strerror", "tdls_version")
-OP_GESV, OP_GETRF, OP_GETRS = 0, 1, 2
-_OPS = {"gesv": OP_GESV, "getrf": OP_GETRF, "getrs": OP_GETRS}
+            "tdls_plan_op", "tdls_posv_batched", "tdls_potrf_batched", "tdls_strerror",
+            "tdls_version")
+OP_GESV, OP_GETRF, OP_GETRS, OP_POTRF, OP_POSV = 0, 1, 2, 3, 4
+_OPS = {"gesv": OP_GESV, "getrf": OP_GETRF, "getrs": OP_GETRS, "potrf": OP_POTRF,
+        "posv": OP_POSV}
 
 
 def library_path() -> str:
@@ -73,6 +75,15 @@ def load_library():
     lib.tdls_getrs_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_potrf_batched.restype = ctypes.c_int
+    lib.tdls_potrf_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_posv_batched.restype = ctypes.c_int
+    lib.tdls_posv_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
     lib.tdls_plan_op.restype = ctypes.c_int
     lib.tdls_plan_op.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int64, ctypes.POINTER(Plan)]
@@ -126,6 +137,20 @@ def tdls_getrs_batched(dtype: int, layout: int, n: int, nrhs: int, batch: int, L
     """The C call itself, raw pointers (ints) in, return code out."""
     return int(load_library().tdls_getrs_batched(int(dtype), int(layout), int(n), int(nrhs),
                                                  int(batch), LU, piv, B, X, stream))
+
+
+def tdls_potrf_batched(dtype: int, layout: int, n: int, batch: int, shift: float, A: int, L: int,
+                       info: int, stream: int) -> int:
+    """The C call itself, raw pointers (ints) in, return code out."""
+    return int(load_library().tdls_potrf_batched(int(dtype), int(layout), int(n), int(batch),
+                                                 float(shift), A, L, info, stream))
+
+
+def tdls_posv_batched(dtype: int, layout: int, n: int, nrhs: int, batch: int, shift: float,
+                      A: int, B: int, X: int, info: int, stream: int) -> int:
+    """The C call itself, raw pointers (ints) in, return code out."""
+    return int(load_library().tdls_posv_batched(int(dtype), int(layout), int(n), int(nrhs),
+                                                int(batch), float(shift), A, B, X, info, stream))
 
 
 def tdls_plan_op(op: int, dtype: int, layout: int, n: int, nrhs: int, batch: int):
@@ -264,3 +289,62 @@ def getrs_batched(LU, piv, B, layout: str = "row", out=None, stream=None):
     if rc != 0:
         raise TdlsError(rc, "tdls_getrs_batched")
     return X
+
+
+def potrf_batched(A, layout: str = "row", shift: float = 0.0, out=None, stream=None):
+    """Cholesky factors of a batch of symmetric matrices: A + shift I = L L^T.
+
+    A: [batch, n, n] in ``layout`` (exactly symmetric, else info = -2).
+    Returns (L, info): L like A, lower triangular with +0.0 above (all +0.0
+    for a failed system); info int32 [batch] (0, j for the first leading
+    minor that is not positive definite, -2).  Does not synchronize.
+    """
+    torch = _torch()
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'row' or 'col'")
+    _check_square(torch, A, "A")
+    batch, n = A.shape[0], A.shape[1]
+    if out is None:
+        L = torch.empty_like(A)
+        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+    else:
+        L, info = out
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        rc = tdls_potrf_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
+                                batch, shift, A.data_ptr(), L.data_ptr(), info.data_ptr(),
+                                s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_potrf_batched")
+    return L, info
+
+
+def posv_batched(A, B, layout: str = "row", shift: float = 0.0, out=None, stream=None):
+    """Solve (A + shift I) X = B by Cholesky for a batch of symmetric
+    positive definite systems.  Shapes as for gesv_batched.  Returns (X,
+    info) with potrf_batched's status; a failed system gets X = +0.0."""
+    torch = _torch()
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'row' or 'col'")
+    _check_square(torch, A, "A")
+    batch, n = A.shape[0], A.shape[1]
+    if B.dtype != A.dtype or not B.is_cuda or B.device != A.device or not B.is_contiguous():
+        raise ValueError("B must be a contiguous CUDA tensor of A's dtype and device")
+    if B.dim() != 3 or B.shape[0] != batch:
+        raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
+    nrhs = B.shape[2] if layout == "row" else B.shape[1]
+    if (B.shape[1] if layout == "row" else B.shape[2]) != n:
+        raise ValueError("B does not match n")
+    if out is None:
+        X = torch.empty_like(B)
+        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+    else:
+        X, info = out
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        rc = tdls_posv_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
+                               nrhs, batch, shift, A.data_ptr(), B.data_ptr(), X.data_ptr(),
+                               info.data_ptr(), s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_posv_batched")
+    return X, info

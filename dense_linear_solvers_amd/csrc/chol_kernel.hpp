@@ -1,0 +1,377 @@
+// Batched Cholesky: (A + shift I) = L L^T, then (posv) L y = b and L^T x = y,
+// one n x n symmetric system per group of T lanes (T = 4, 16 or 64) of a
+// wave64, lane tx holding the fixed rows tx, tx+T, ... in VGPRs.
+//
+// What is computed (cited by page title and section):
+//  * "ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged
+//    numerical and failure contract: the Cholesky inner products accumulate
+//    in increasing k and only independent rows run in parallel; the diagonal
+//    shift is explicit and nothing else is added; status 0, the first failed
+//    pivot (positive), -2 for a matrix that is not symmetric; a failed
+//    system's factors and solutions are all zero; inputs read only.
+//  * "cuSolverDx potrf" function page: the status of a failed factorization
+//    is the smallest leading minor that is not positive definite (1-based);
+//    L is lower triangular.
+//
+// Order of the arithmetic, element by element: a(i,j) gets fma(-L(i,k),
+// L(j,k), .) for k = 0, 1, ..., j-1 in that order (here applied right-looking,
+// one k per step, which is the same sequence of fused multiply-adds as the
+// left-looking inner product), the diagonal starts from A(j,j) + shift
+// rounded once, L(j,j) = sqrt of it, L(i,j) = a(i,j) / L(j,j) by IEEE
+// division.  The forward substitution is folded into the steps (y_j / L(j,j),
+// then y_j leaves the rows below); the back substitution takes x_j =
+// y_j / L(j,j) for j = n-1 .. 0 and removes it from the rows above.
+//
+// gfx950 design.  There is no pivot search: row r stays in lane r % T, slot
+// r / T.  The column of multipliers just formed is itself the broadcast
+// source of the rank-1 update: L(c,j) sits in lane c % T, slot c / T, which
+// is the lane a DPP row_newbcast (T = 16) or quad_perm (T = 4) reads, or a
+// readlane (T = 64) — no exchange through LDS.  Only slots that hold rows
+// at or below column c take the update of column c.  The symmetry check and
+// the back substitution read a row-major copy of the matrix (then of L) in
+// LDS with an odd row stride.
+#pragma once
+
+#include "gesv_panel.hpp"
+
+namespace tdls {
+
+template <typename Real, int N, int NRHS, int T>
+struct CholShape {
+  static_assert(T == 4 || T == 16 || T == 64, "Cholesky groups are 4, 16 or 64 lanes");
+  static constexpr int R = (N + T - 1) / T;
+  static constexpr int G = kWaveSize / T;
+  static constexpr int SL = T < 16 ? T : 16;
+  static constexpr int S = N + 1;   // LDS row stride (odd: no bank conflicts)
+  static constexpr int VEC = RealTraits<Real>::VEC;
+  static constexpr int GROUP_ELEMS = (N * S + VEC - 1) / VEC * VEC;
+  static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
+  static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
+};
+
+// Value of `v` on lane L of the caller's group (T = 4, 16) or of the wave
+// (T = 64).
+template <int T, int L>
+__device__ __forceinline__ double group_bcast(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  uint32_t lo, hi;
+  if constexpr (T == 64) {
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, L);
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), L);
+  } else if constexpr (T == 16) {
+    lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0x150 + L, 0xf, 0xf, true);
+    hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0x150 + L, 0xf, 0xf, true);
+  } else {
+    constexpr int qp = L | (L << 2) | (L << 4) | (L << 6);
+    lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, qp, 0xf, 0xf, true);
+    hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), qp, 0xf, 0xf, true);
+  }
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int T, int L>
+__device__ __forceinline__ float group_bcast(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (T == 64)
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, L));
+  else if constexpr (T == 16)
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x150 + L, 0xf, 0xf, true));
+  else
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(b, L | (L << 2) | (L << 4) | (L << 6), 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ double sqrt_ieee(double v) { return __builtin_sqrt(v); }
+__device__ __forceinline__ float sqrt_ieee(float v) { return __builtin_sqrtf(v); }
+
+// FACT = false: posv, X receives the solutions.  FACT = true: potrf (NRHS
+// must be 1, Bm is not read), X receives L in the layout of A, zero above
+// the diagonal.
+template <typename Real, int N, int NRHS, int T, bool FACT>
+__global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
+    chol_kernel(int col, int n, int nrhs, int64_t batch, Real shift, const Real* __restrict__ A,
+                const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ info) {
+  static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
+  using S = CholShape<Real, N, NRHS, T>;
+  constexpr int R = S::R;
+  constexpr int G = S::G;
+  constexpr int SL = S::SL;
+  constexpr int ST = S::S;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x / kWaveSize;
+  const int g = lane / T;
+  const int tx = lane & (T - 1);
+  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * G;
+  if (wave_first >= batch) return;  // the whole wave is past the batch
+  const int64_t sys = wave_first + g;
+  const bool live = sys < batch;
+  Real* sq = reinterpret_cast<Real*>(lds_raw + wave * S::WAVE_BYTES) + g * S::GROUP_ELEMS;
+
+  // ---- load: row q = tx + K*T of A and of B; past n the identity and zero
+  Real a[R][N];
+  Real y[R][NRHS];
+  {
+    const Real* As = A + (live ? sys : 0) * (int64_t)n * n;
+    const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
+    if (n == N && nrhs == NRHS) {
+      // the kernel's own size: compile-time offsets from one base per row
+      auto load_exact = [&](auto colc) {
+        constexpr bool COL = decltype(colc)::value;
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const int q = tx + K * T;
+          const int qq = live && q < n ? q : 0;
+          const Real* ar = As + (COL ? qq : qq * N);
+          const Real* br = Bs + (COL ? qq : qq * NRHS);
+          sfor<0, N>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            a[K][c] = ar[COL ? c * N : c];
+          });
+          sfor<0, NRHS>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (FACT)
+              y[K][j] = Real(0);
+            else
+              y[K][j] = br[COL ? j * N : j];
+          });
+        });
+      };
+      if (col)
+        load_exact(std::true_type{});
+      else
+        load_exact(std::false_type{});
+    } else {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        const bool qrow = live && q < n;
+        const int qq = qrow ? q : 0;
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          a[K][c] = (q == c) ? Real(1) : Real(0);
+          if (qrow && c < n) a[K][c] = As[col ? (int64_t)c * n + qq : (int64_t)qq * n + c];
+        });
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          y[K][j] = Real(0);
+          if constexpr (!FACT)
+            if (qrow && j < nrhs) y[K][j] = Bs[col ? (int64_t)j * n + qq : (int64_t)qq * nrhs + j];
+        });
+      });
+    }
+  }
+
+  // ---- exact symmetry: every row is written to LDS, lane tx compares its
+  // row q with column q read back
+  bool asym = false;
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    const int q = tx + K * T;
+    if (q < N) {
+      sfor<0, N>([&](auto cc) { sq[q * ST + decltype(cc)::value] = a[K][decltype(cc)::value]; });
+    }
+  });
+  wave_sync_lds();
+  sfor<0, R>([&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    const int q = tx + K * T;
+    const int qq = q < N ? q : N - 1;
+    sfor<0, N>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      asym = asym | ((q < N) & !(sq[c * ST + qq] == a[K][c]));   // phantom rows excluded
+    });
+  });
+  wave_sync_lds();   // the copy is rewritten below
+  int status;
+  {
+    // one status per group: any lane of the group that saw a mismatch
+    const uint64_t m = __builtin_amdgcn_ballot_w64(asym);
+    uint64_t gm;
+    if constexpr (T == 64)
+      gm = m;
+    else
+      gm = (m >> (g * T)) & ((1ull << T) - 1ull);
+    status = gm != 0 ? -2 : 0;
+  }
+
+  // ---- the explicit diagonal shift, added once to A(q,q)
+  if (shift != Real(0)) {
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      sfor<0, N>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if constexpr (c >= K * T && c < (K + 1) * T)
+          a[K][c] = (q == c && q < n) ? a[K][c] + shift : a[K][c];
+      });
+    });
+  }
+
+  // ---- factorization with the forward substitution folded in
+  sfor<0, N>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int js = j / T;
+    constexpr int jl = j % T;
+    constexpr int BL = T == 64 ? jl : jl % SL;   // lane of row j in the broadcast domain
+    const Real s = group_bcast<T, BL>(a[js][j]);
+    const bool bad = !(s > Real(0));
+    if (bad && status == 0) status = j + 1;
+    asm volatile("" : "+v"(status));   // settled now, not at the store
+    const Real d = bad ? Real(1) : sqrt_ieee(s);
+    // multipliers of the rows below j; row j itself takes d
+    Real lm[R];
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      if constexpr (K < js) {
+        lm[K] = Real(0);
+      } else {
+        const Real l = a[K][j] / d;
+        if constexpr (K > js) {
+          lm[K] = l;
+          a[K][j] = l;
+        } else {
+          lm[K] = tx > jl ? l : Real(0);
+          a[K][j] = tx > jl ? l : (tx == jl ? d : a[K][j]);
+        }
+        asm volatile("" : "+v"(a[K][j]));
+      }
+    });
+    // forward substitution: y_j / d on its lane, then y_j leaves the rows below
+    sfor<0, NRHS>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      if constexpr (!FACT) {
+        const Real yj = y[js][r] / d;
+        y[js][r] = tx == jl ? yj : y[js][r];
+        const Real yb = group_bcast<T, BL>(y[js][r]);
+        sfor<js, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          y[K][r] = __builtin_fma(-lm[K], yb, y[K][r]);
+        });
+      }
+    });
+    // rank-1 update of the columns right of j, on the slots holding rows at
+    // or below each column; L(c, j) comes from lane c % T, slot c / T
+    sfor<j + 1, N>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int cs = c / T;
+      constexpr int cl = c % T;
+      if constexpr (T <= 16) {
+        sfor<cs, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          // the first read of each source register after its write above
+          // needs the DPP wait states
+          if constexpr (K >= js)
+            fnmac_bcast<T, cl % SL, K == cs && (c == j + 1 || cl == 0)>(a[K][c], a[cs][j],
+                                                                        lm[K]);
+        });
+      } else {
+        const Real lc = group_bcast<T, cl>(a[cs][j]);
+        sfor<cs, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          if constexpr (K >= js) a[K][c] = __builtin_fma(-lm[K], lc, a[K][c]);
+        });
+      }
+    });
+  });
+
+  const bool failed = status != 0;
+  if constexpr (FACT) {
+    // ---- L in the layout of A, zero above the diagonal; zero when failed
+    if (live) {
+      Real* Ls = X + sys * ((int64_t)n * n);
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        if (q < n) {
+          auto store_row = [&](auto colc, auto exactc) {
+            constexpr bool COL = decltype(colc)::value;
+            constexpr bool EXACT = decltype(exactc)::value;
+            const int64_t ld = EXACT ? N : n;
+            Real* rowp = Ls + (COL ? (int64_t)q : (int64_t)q * ld);
+            sfor<0, N>([&](auto cc) {
+              constexpr int c = decltype(cc)::value;
+              const Real v = (failed || c > q) ? Real(0) : a[K][c];
+              if (EXACT || c < n) rowp[COL ? c * ld : c] = v;
+              if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+            });
+          };
+          if (n == N) {
+            if (col)
+              store_row(std::true_type{}, std::true_type{});
+            else
+              store_row(std::false_type{}, std::true_type{});
+          } else {
+            if (col)
+              store_row(std::true_type{}, std::false_type{});
+            else
+              store_row(std::false_type{}, std::false_type{});
+          }
+        }
+      });
+      if (tx == 0) info[sys] = status;
+    }
+  } else {
+    // ---- L^T x = y: L by rows into LDS, then x_j = y_j / L(j,j) on its
+    // lane, removed from the rows above with L(j,q) read at row j, column q
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      if (q < N) {
+        sfor<0, N>([&](auto cc) { sq[q * ST + decltype(cc)::value] = a[K][decltype(cc)::value]; });
+      }
+    });
+    wave_sync_lds();
+    Real xr[R][NRHS];
+    sfor<0, R>([&](auto Kc) {
+      sfor<0, NRHS>([&](auto rc) { xr[decltype(Kc)::value][decltype(rc)::value] = Real(0); });
+    });
+    sfor<0, N>([&](auto ic) {
+      constexpr int j = N - 1 - decltype(ic)::value;
+      constexpr int js = j / T;
+      constexpr int jl = j % T;
+      __builtin_amdgcn_sched_barrier(0);
+      Real lj[js + 1];
+      sfor<0, js + 1>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        lj[K] = sq[j * ST + (q < N ? q : N - 1)];   // L(j, q), meaningful for q < j
+      });
+      const Real djj = a[js][j];
+      sfor<0, NRHS>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const Real x = y[js][r] / djj;   // meaningful on lane jl
+        xr[js][r] = tx == jl ? x : xr[js][r];
+        asm volatile("" : "+v"(xr[js][r]));
+        constexpr int BL = T == 64 ? jl : jl % SL;
+        const Real xb = group_bcast<T, BL>(x);
+        sfor<0, js + 1>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          y[K][r] = __builtin_fma(-lj[K], xb, y[K][r]);
+        });
+      });
+    });
+    if (live) {
+      Real* Xs = X + sys * ((int64_t)n * nrhs);
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        if (q < n) {
+          sfor<0, NRHS>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            if (r < nrhs) {
+              const Real v = failed ? Real(0) : xr[K][r];
+              if (col)
+                Xs[(int64_t)r * n + q] = v;
+              else
+                Xs[(int64_t)q * nrhs + r] = v;
+            }
+          });
+        }
+      });
+      if (tx == 0) info[sys] = status;
+    }
+  }
+}
+
+}  // namespace tdls

@@ -4,6 +4,7 @@
 // parallel.
 #include "gesv_panel.hpp"
 #include "getrs_kernel.hpp"
+#include "chol_kernel.hpp"
 
 #if !defined(TDLS_INST_SFX) || !defined(TDLS_INST_REAL) || !defined(TDLS_INST_N) || \
     !defined(TDLS_INST_NRHS)
@@ -51,6 +52,25 @@ static int launch_getrs(const LaunchPlan& p, const void* LU, const void* B, void
   return (int)hipGetLastError();
 }
 
+template <typename Real, int N, int NRHS, int T, bool FACT>
+static int launch_chol(const LaunchPlan& p, const void* A, const void* B, void* X,
+                       int32_t* info, hipStream_t stream) {
+  if constexpr (T == 32) {
+    return (int)hipErrorInvalidConfiguration;   // no Cholesky kernel for 32-lane groups
+  } else {
+    using S = CholShape<Real, N, NRHS, T>;
+    static_assert(S::BLOCK_BYTES == chol_lds_bytes(N, T, sizeof(Real) == 8),
+                  "host and device LDS sizes disagree");
+    static_assert(S::BLOCK_BYTES <= 65536, "Cholesky LDS stays within the default limit");
+    if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((chol_kernel<Real, N, NRHS, T, FACT>), dim3((unsigned)p.grid),
+                       dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
+                       p.batch, (Real)p.shift, static_cast<const Real*>(A),
+                       static_cast<const Real*>(B), static_cast<Real*>(X), info);
+    return (int)hipGetLastError();
+  }
+}
+
 template <typename Real, int N, int NRHS, int T>
 static int launch_op(const LaunchPlan& p, const void* in0, const void* in1, void* out,
                      int32_t* piv, int32_t* info, hipStream_t stream) {
@@ -64,6 +84,13 @@ static int launch_op(const LaunchPlan& p, const void* in0, const void* in1, void
         return (int)hipErrorInvalidConfiguration;
     case kOpGetrs:
       return launch_getrs<Real, N, NRHS, T>(p, in0, in1, out, piv, stream);
+    case kOpPotrf:
+      if constexpr (NRHS == 1)
+        return launch_chol<Real, N, NRHS, T, true>(p, in0, nullptr, out, info, stream);
+      else
+        return (int)hipErrorInvalidConfiguration;
+    case kOpPosv:
+      return launch_chol<Real, N, NRHS, T, false>(p, in0, in1, out, info, stream);
     default:
       return (int)hipErrorInvalidConfiguration;
   }

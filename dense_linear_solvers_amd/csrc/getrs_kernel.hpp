@@ -90,17 +90,17 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   {
     const Real* Ls = LU + (live ? sys : 0) * (int64_t)n * n;
     const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      const bool qrow = live && q < n;
-      const int qq = qrow ? q : 0;
-      const int sr = src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]);
-      if (n == N && nrhs == NRHS) {
-        // the kernel's own size: compile-time offsets from one base per row
-        // (a row-major row is one run of vector loads)
-        auto load_exact = [&](auto colc) {
-          constexpr bool COL = decltype(colc)::value;
+    auto src_row = [&](int K) { return src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]); };
+    if (n == N && nrhs == NRHS) {
+      // the kernel's own size: compile-time offsets from one base per row
+      // (a row-major row is one run of vector loads)
+      auto load_exact = [&](auto colc) {
+        constexpr bool COL = decltype(colc)::value;
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const int q = tx + K * T;
+          const int qq = live && q < n ? q : 0;
+          const int sr = src_row(K);
           const Real* lr = Ls + (COL ? qq : qq * N);
           const Real* br = Bs + (COL ? sr : sr * NRHS);
           sfor<0, N>([&](auto cc) {
@@ -111,12 +111,19 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             constexpr int j = decltype(jc)::value;
             y[K][j] = q < N ? br[COL ? j * N : j] : Real(0);
           });
-        };
-        if (col)
-          load_exact(std::true_type{});
-        else
-          load_exact(std::false_type{});
-      } else {
+        });
+      };
+      if (col)
+        load_exact(std::true_type{});
+      else
+        load_exact(std::false_type{});
+    } else {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        const bool qrow = live && q < n;
+        const int qq = qrow ? q : 0;
+        const int sr = src_row(K);
         sfor<0, N>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           a[K][c] = (q == c) ? Real(1) : Real(0);
@@ -127,8 +134,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           y[K][j] = Real(0);
           if (qrow && j < nrhs) y[K][j] = Bs[col ? (int64_t)j * n + sr : (int64_t)sr * nrhs + j];
         });
-      }
-    });
+      });
+    }
   }
 
   // ---- L y = P b: y_k (lane k % T, slot k / T) leaves the rows below it.

@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 
 #include "../../include/tdls.h"
 #include "tdls_internal.h"
@@ -91,7 +92,10 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   p->systems_per_block = (int64_t)kWavesPerBlock * p->G;
   p->grid = (batch + p->systems_per_block - 1) / p->systems_per_block;
   if (p->grid > 0x7fffffffLL) return -5;
-  p->lds_bytes = op == kOpGetrs ? getrs_lds_bytes(N, T) : gesv_lds_bytes(N, NRHS, T, is64);
+  p->shift = 0.0;
+  p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, T)
+                 : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, T, is64)
+                                                     : gesv_lds_bytes(N, NRHS, T, is64);
   return 0;
 }
 
@@ -158,10 +162,12 @@ int tdls_plan_gesv(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_
 
 int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nrhs,
                  int64_t batch, tdls_plan* out) {
-  if (op != TDLS_OP_GESV && op != TDLS_OP_GETRF && op != TDLS_OP_GETRS) return -1;
+  if (op != TDLS_OP_GESV && op != TDLS_OP_GETRF && op != TDLS_OP_GETRS && op != TDLS_OP_POTRF &&
+      op != TDLS_OP_POSV)
+    return -1;
   tdls::LaunchPlan p;
-  int rc = tdls::make_plan((int)op, (int)dtype, (int)layout, n, op == TDLS_OP_GETRF ? 1 : nrhs,
-                           batch, &p);
+  const bool factor = op == TDLS_OP_GETRF || op == TDLS_OP_POTRF;
+  int rc = tdls::make_plan((int)op, (int)dtype, (int)layout, n, factor ? 1 : nrhs, batch, &p);
   if (rc != 0) return rc < 0 ? rc - 1 : rc;   // argument numbers shift by one
   rc = tdls::fill_plan(p, out);
   return rc == -6 ? -7 : rc;
@@ -241,6 +247,52 @@ int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, in
   return tdls::launch(p, LU, B, X, const_cast<int32_t*>(piv), nullptr, stream);
 }
 
+int tdls_potrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, double shift,
+                       const void* A, void* L, int32_t* info, hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpPotrf, (int)dtype, (int)layout, n, 1, batch, &p);
+  if (rc == -5) return -4;   // batch is argument 4 here
+  if (rc != 0) return rc;
+  if (!std::isfinite(shift)) return -5;
+  if (batch == 0) return TDLS_SUCCESS;
+  p.shift = shift;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesA = (size_t)batch * n * n * es;
+  const size_t bytesI = (size_t)batch * 4;
+  if (A == nullptr || tdls::misaligned(A, es)) return -6;
+  if (L == nullptr || tdls::misaligned(L, es) || tdls::overlaps(L, bytesA, A, bytesA)) return -7;
+  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
+      tdls::overlaps(info, bytesI, L, bytesA))
+    return -8;
+  return tdls::launch(p, A, nullptr, L, nullptr, info, stream);
+}
+
+int tdls_posv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                      double shift, const void* A, const void* B, void* X, int32_t* info,
+                      hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpPosv, (int)dtype, (int)layout, n, nrhs, batch, &p);
+  if (rc != 0) return rc;
+  if (!std::isfinite(shift)) return -6;
+  if (batch == 0) return TDLS_SUCCESS;
+  p.shift = shift;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesA = (size_t)batch * n * n * es;
+  const size_t bytesB = (size_t)batch * n * nrhs * es;
+  const size_t bytesI = (size_t)batch * 4;
+  if (A == nullptr || tdls::misaligned(A, es)) return -7;
+  if (B == nullptr || tdls::misaligned(B, es)) return -8;
+  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, A, bytesA) ||
+      tdls::overlaps(X, bytesB, B, bytesB))
+    return -9;
+  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
+      tdls::overlaps(info, bytesI, B, bytesB) || tdls::overlaps(info, bytesI, X, bytesB))
+    return -10;
+  return tdls::launch(p, A, B, X, nullptr, info, stream);
+}
+
 const char* tdls_strerror(int code) {
   switch (code) {
     case TDLS_SUCCESS: return "success";
@@ -248,8 +300,8 @@ const char* tdls_strerror(int code) {
     case -2: return "argument 2 is invalid (layout, or dtype for tdls_plan_op)";
     case -3: return "argument 3 is invalid (n outside 1..64, or layout for tdls_plan_op)";
     case -4: return "argument 4 is invalid (nrhs outside 1..8; batch for getrf; n for plan_op)";
-    case -5: return "argument 5 is invalid (batch; A for getrf; nrhs for plan_op)";
-    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; batch for plan_op)";
+    case -5: return "argument 5 is invalid (batch; A for getrf; shift for potrf; nrhs for plan_op)";
+    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; shift for posv; batch for plan_op)";
     case -7: return "argument 7 is invalid (null, misaligned or overlapping buffer)";
     case -8: return "argument 8 is invalid (null, misaligned or overlapping buffer)";
     case -9: return "argument 9 is invalid (null, misaligned or overlapping buffer)";

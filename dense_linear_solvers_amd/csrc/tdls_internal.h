@@ -38,7 +38,7 @@ constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 1;
 
 // Operations the library launches.
-enum OpKind : int { kOpGesv = 0, kOpGetrf = 1, kOpGetrs = 2 };
+enum OpKind : int { kOpGesv = 0, kOpGetrf = 1, kOpGetrs = 2, kOpPotrf = 3, kOpPosv = 4 };
 
 // Everything a launch needs, decided on the host before any launch.
 struct LaunchPlan {
@@ -51,6 +51,7 @@ struct LaunchPlan {
   int R;              // rows per lane, ceil(N / T)
   int G;              // systems per wave, 64 / T
   int64_t batch;
+  double shift;       // Cholesky: explicit diagonal shift (0 otherwise)
   int64_t systems_per_block;
   int64_t grid;
   int threads_per_block;
@@ -107,12 +108,23 @@ constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
 // of each group.
 constexpr int getrs_lds_bytes(int N, int T) { return kWavesPerBlock * (kWaveSize / T) * N * 4; }
 
+// LDS bytes of one block (one wave) of the Cholesky kernel: a row-major copy
+// of each group's matrix with an odd row stride (N + 1), rounded up to 16
+// bytes.
+constexpr int chol_lds_bytes(int N, int T, bool is64) {
+  const int es = is64 ? 8 : 4;
+  const int vec = 16 / es;
+  return kWavesPerBlock * (kWaveSize / T) * ((N * (N + 1) + vec - 1) / vec * vec) * es;
+}
+
 // Launchers, one per shape of TDLS_FOR_EACH_SHAPE, defined in the
 // instantiation translation units.  They enqueue the kernel of p.op and p.T
 // and return a hipError_t value cast to int.  Operands by op:
 //   gesv:  in0 = A, in1 = B, out = X, piv and info written;
 //   getrf: in0 = A, out = LU, piv and info written (NRHS = 1 shapes only);
-//   getrs: in0 = LU, in1 = B, out = X, piv read, info unused.
+//   getrs: in0 = LU, in1 = B, out = X, piv read, info unused;
+//   potrf: in0 = A, out = L, info written (NRHS = 1 shapes only);
+//   posv:  in0 = A, in1 = B, out = X, info written.
 using GesvLauncher = int (*)(const LaunchPlan& p, const void* in0, const void* in1, void* out,
                              int32_t* piv, int32_t* info, hipStream_t stream);
 #define TDLS_DECLARE_LAUNCHER(sfx, Real, N, NRHS)                                              \

@@ -26,6 +26,17 @@ recipe's modifications):
   n64_f64_row      n=64, nrhs=8, batch=131072,    float64, row-major,
                    A iid N(0, 1) plus 0.5 on the diagonal; B iid N(0, 1).
 
+Symmetric positive definite recipes for the Cholesky path (the same shapes
+as three of the above):
+
+  spd_n16_f32_row  n=16, nrhs=4, batch=65536,  float32, row-major
+  spd_n32_f64_col  n=32, nrhs=1, batch=262144, float64, column-major
+  spd_n64_f64_row  n=64, nrhs=8, batch=131072, float64, row-major
+                   G iid N(0, 1) [batch, n, n], A = G G^T / n + I in
+                   float64, rounded to the working dtype and made exactly
+                   symmetric (the upper triangle mirrors the lower); B iid
+                   N(0, 1), drawn after G.
+
 Every recipe accepts a smaller ``batch`` for quick runs: the draws are then
 the first systems of the same kind of stream, not a prefix of the full batch.
 """
@@ -36,7 +47,8 @@ from typing import Callable, Optional
 
 import numpy as np
 
-__all__ = ["Workload", "RECIPES", "make", "logical_to_storage", "rhs_logical_to_storage"]
+__all__ = ["Workload", "RECIPES", "SPD_RECIPES", "make", "logical_to_storage",
+           "rhs_logical_to_storage"]
 
 
 @dataclass(frozen=True)
@@ -64,6 +76,18 @@ RECIPES = {
                "A iid U(-1,1), row i scaled by 10**U(-3,3); B iid U(-1,1)"),
         Recipe("n64_f64_row", 64, 8, 131072, "f64", "row", "normal",
                "A iid N(0,1) + 0.5 I; B iid N(0,1)"),
+    )
+}
+
+SPD_RECIPES = {
+    r.name: r
+    for r in (
+        Recipe("spd_n16_f32_row", 16, 4, 65536, "f32", "row", "normal",
+               "A = G G^T / n + I, G iid N(0,1), exactly symmetric; B iid N(0,1)"),
+        Recipe("spd_n32_f64_col", 32, 1, 262144, "f64", "col", "normal",
+               "A = G G^T / n + I, G iid N(0,1), exactly symmetric; B iid N(0,1)"),
+        Recipe("spd_n64_f64_row", 64, 8, 131072, "f64", "row", "normal",
+               "A = G G^T / n + I, G iid N(0,1), exactly symmetric; B iid N(0,1)"),
     )
 }
 
@@ -120,6 +144,8 @@ def make(name: str, seed: int = 0, batch: Optional[int] = None,
     stream until none is left.  Without it no system is redrawn, and
     ``meta["gap_filtered"]`` says so.
     """
+    if name in SPD_RECIPES:
+        return _make_spd(name, seed, batch)
     r = RECIPES[name]
     b = r.batch if batch is None else int(batch)
     n, nrhs = r.n, r.nrhs
@@ -170,3 +196,25 @@ def make(name: str, seed: int = 0, batch: Optional[int] = None,
         meta["redrawn"] = redrawn
 
     return Workload(name, n, nrhs, b, r.dtype, r.layout, A_st, B_st, meta)
+
+
+def _make_spd(name: str, seed: int, batch: Optional[int]) -> Workload:
+    r = SPD_RECIPES[name]
+    b = r.batch if batch is None else int(batch)
+    n, nrhs = r.n, r.nrhs
+    wdt = np.float32 if r.dtype == "f32" else np.float64
+    rng = np.random.default_rng(seed)
+    G = _draw(rng, "normal", (b, n, n))
+    B = _draw(rng, "normal", (b, n, nrhs)).astype(wdt)
+    A = np.empty((b, n, n), dtype=wdt)
+    chunk = 1 << 14
+    for s0 in range(0, b, chunk):
+        g = G[s0:s0 + chunk]
+        m = (g @ g.transpose(0, 2, 1)) / n + np.eye(n)
+        m = m.astype(wdt)
+        low = np.tril(m)
+        A[s0:s0 + chunk] = low + np.tril(m, -1).transpose(0, 2, 1)
+    del G
+    meta = {"recipe": r.note, "seed": seed}
+    return Workload(name, n, nrhs, b, r.dtype, r.layout, logical_to_storage(A, r.layout),
+                    rhs_logical_to_storage(B, r.layout), meta)

@@ -54,7 +54,9 @@ typedef enum tdls_layout {
 typedef enum tdls_op {
   TDLS_OP_GESV = 0,  /* factor and solve in one call (tdls_gesv_batched) */
   TDLS_OP_GETRF = 1, /* factor only (tdls_getrf_batched) */
-  TDLS_OP_GETRS = 2  /* solve from factors (tdls_getrs_batched) */
+  TDLS_OP_GETRS = 2, /* solve from factors (tdls_getrs_batched) */
+  TDLS_OP_POTRF = 3, /* Cholesky factor (tdls_potrf_batched) */
+  TDLS_OP_POSV = 4   /* Cholesky factor and solve (tdls_posv_batched) */
 } tdls_op;
 
 /* Return codes of the calls (not the per-system status, see `info`). */
@@ -200,9 +202,58 @@ int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, in
                        hipStream_t stream);
 
 /*
+ * Cholesky factorization A_s + shift I = L_s L_s^T of symmetric positive
+ * definite matrices, s = 0 .. batch-1 (LAPACK's potrf, lower).
+ *
+ * Contract ("ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged
+ * numerical and failure contract; "cuSolverDx potrf" function page):
+ *   - A must be exactly symmetric in the working precision (A(i,j) ==
+ *     A(j,i) for every pair), else info = -2;
+ *   - the shift is explicit: the diagonal is A(j,j) + shift, rounded once,
+ *     and nothing else is added;
+ *   - inner products accumulate in increasing k, one fused multiply-add per
+ *     term; L(j,j) is the IEEE square root, L(i,j) an IEEE quotient;
+ *   - info = j >= 1 for the smallest leading minor that is not positive
+ *     definite (the first step whose diagonal is not > 0), else 0;
+ *   - a failed system (info != 0) gets L = +0.0 everywhere.
+ *
+ * Arguments (-i on rejection):
+ *   [1] dtype, [2] layout, [3] n (1..64): as for tdls_gesv_batched.
+ *   [4] batch   >= 0; 0 launches nothing.
+ *   [5] shift   finite diagonal shift (0 for none), rounded to dtype.
+ *   [6] A       device, batch * n * n elements; read only.
+ *   [7] L       device, batch * n * n elements, layout of A; written: L on
+ *               and below the diagonal, +0.0 above; must not overlap A.
+ *   [8] info    device, int32 [batch]; written.
+ *       stream  HIP stream.
+ * Ownership, stream semantics and errors as for tdls_gesv_batched.
+ */
+int tdls_potrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, double shift,
+                       const void* A, void* L, int32_t* info, hipStream_t stream);
+
+/*
+ * Solve (A_s + shift I) X_s = B_s by Cholesky (LAPACK's posv): the
+ * factorization of tdls_potrf_batched with L y = b folded into its steps,
+ * then L^T x = y, each x_j = y_j / L(j,j) by IEEE division and removed from
+ * the rows above by fused multiply-adds.  Same status; a failed system
+ * gets X = +0.0.
+ *
+ * Arguments (-i on rejection):
+ *   [1] dtype, [2] layout, [3] n (1..64), [4] nrhs (1..8), [5] batch.
+ *   [6] shift   finite diagonal shift.
+ *   [7] A       device, read only.  [8] B  device, read only.
+ *   [9] X       device, like B; must not overlap A or B.
+ *  [10] info    device, int32 [batch].
+ *       stream  HIP stream.
+ */
+int tdls_posv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                      double shift, const void* A, const void* B, void* X, int32_t* info,
+                      hipStream_t stream);
+
+/*
  * tdls_plan_gesv for any operation: [1] op, then the scalar arguments of
  * tdls_plan_gesv shifted by one ([2] dtype ... [6] batch, [7] out); nrhs is
- * ignored for TDLS_OP_GETRF.  Host only.
+ * ignored for TDLS_OP_GETRF and TDLS_OP_POTRF.  Host only.
  */
 int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nrhs,
                  int64_t batch, tdls_plan* out);

@@ -194,3 +194,34 @@ def test_factor_solve_pointer_validation(lib):
     assert s(lu, pv, b, lu) == -9                # X overlaps LU
     assert tdls.tdls_getrf_batched(tdls.F64, tdls.ROW_MAJOR, n, 0, 0, 0, 0, 0, 0) == 0
     assert tdls.tdls_getrs_batched(tdls.F64, tdls.ROW_MAJOR, n, 1, 0, 0, 0, 0, 0, 0) == 0
+
+
+def test_cholesky_validation_before_launch(lib):
+    n, nrhs, batch = 16, 2, 10
+    es = 8
+    a = 1 << 40                                  # never dereferenced: every call fails
+    l = a + batch * n * n * es                   # before the device is queried
+    inf = l + batch * n * n * es
+    b = inf + batch * 4 + 64
+    x = b + batch * n * nrhs * es
+    assert tdls.tdls_potrf_batched(7, 0, n, batch, 0.0, a, l, inf, 0) == -1
+    assert tdls.tdls_potrf_batched(0, 0, 65, batch, 0.0, a, l, inf, 0) == -3
+    assert tdls.tdls_potrf_batched(0, 0, n, -1, 0.0, a, l, inf, 0) == -4
+    f = lambda shift, *p: tdls.tdls_potrf_batched(tdls.F64, tdls.ROW_MAJOR, n, batch, shift, *p, 0)
+    assert f(float("nan"), a, l, inf) == -5
+    assert f(0.0, 0, l, inf) == -6
+    assert f(0.0, a, a, inf) == -7
+    assert f(0.0, a, l, l) == -8
+    s = lambda shift, *p: tdls.tdls_posv_batched(tdls.F64, tdls.COL_MAJOR, n, nrhs, batch, shift,
+                                                 *p, 0)
+    assert tdls.tdls_posv_batched(0, 0, n, 0, batch, 0.0, a, b, x, inf, 0) == -4
+    assert tdls.tdls_posv_batched(0, 0, n, 1, -1, 0.0, a, b, x, inf, 0) == -5
+    assert s(float("-inf"), a, b, x, inf) == -6
+    assert s(0.0, 0, b, x, inf) == -7
+    assert s(0.0, a, 0, x, inf) == -8
+    assert s(0.0, a, b, a, inf) == -9
+    assert s(0.0, a, b, x, x) == -10
+    assert tdls.tdls_posv_batched(tdls.F64, tdls.ROW_MAJOR, n, 1, 0, 0.0, 0, 0, 0, 0, 0) == 0
+    p = tdls.plan_op("posv", "f64", "col", 32, 1, 1000)
+    assert p["lds_bytes"] == p["systems_per_wave"] * 32 * 33 * 8
+    assert tdls.plan_op("potrf", "f32", "row", 13, 5, 10)["nrhs_kernel"] == 1

@@ -1,0 +1,232 @@
+"""GPU parity of the Cholesky path (potrf, posv) through the C interface vs
+the CPU oracle.
+
+Bar: info bit-exact (0, j for the first non-positive pivot, -2 for a matrix
+that is not exactly symmetric); factors within the normwise tolerance of the
+working precision (1e-11 float64, 1e-4 float32, as max |L - L_oracle| /
+max |L_oracle|) and all +0.0 when failed; solutions within the normwise
+tolerance on kappa <= 1e3 systems, scaled residual <= 10, all +0.0 when
+failed.  Exactly representable problems (integer factors) must come out
+exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import metrics
+import oracle
+import parity
+import dense_linear_solvers_amd as tdls
+from dense_linear_solvers_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np(dt):
+    return np.float32 if dt == "f32" else np.float64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tdls.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_potrf(A_st, layout, shift=0.0):
+    A = torch.from_numpy(np.ascontiguousarray(A_st)).to(DEV)
+    L, info = tdls.potrf_batched(A, layout, shift)
+    torch.cuda.synchronize()
+    return L.cpu().numpy(), info.cpu().numpy()
+
+
+def gpu_posv(A_st, B_st, layout, shift=0.0):
+    A = torch.from_numpy(np.ascontiguousarray(A_st)).to(DEV)
+    B = torch.from_numpy(np.ascontiguousarray(B_st)).to(DEV)
+    X, info = tdls.posv_batched(A, B, layout, shift)
+    torch.cuda.synchronize()
+    return X.cpu().numpy(), info.cpu().numpy()
+
+
+def spd(rng, batch, n, dtype, shift_diag=1.0):
+    G = rng.standard_normal((batch, n, n))
+    A = (G @ G.transpose(0, 2, 1)) / n + shift_diag * np.eye(n)
+    A = A.astype(dtype)
+    return np.tril(A) + np.tril(A, -1).transpose(0, 2, 1)
+
+
+def check(A_l, B_l, layout, shift=0.0, what=""):
+    """Run potrf and posv on logical A, B; compare with the oracle."""
+    dt = np.dtype(A_l.dtype)
+    n, nrhs = A_l.shape[1], B_l.shape[2]
+    A_st = oracle.to_storage(A_l, layout)
+    B_st = oracle.rhs_to_storage(B_l, layout)
+    Lg, ig = gpu_potrf(A_st, layout, shift)
+    Lo, io = oracle.potrf(A_st, n, layout, shift)
+    np.testing.assert_array_equal(ig, io, err_msg=f"{what}: potrf info")
+    Lg = oracle.from_storage(Lg, layout, n)
+    ok = io == 0
+    assert (Lg[~ok] == 0).all() and not np.signbit(Lg[~ok]).any(), what
+    assert (np.triu(Lg, 1) == 0).all(), f"{what}: L not lower triangular"
+    if ok.any():
+        num = np.abs(Lg[ok].astype(np.float64) - Lo[ok]).max(axis=(1, 2))
+        den = np.abs(Lo[ok].astype(np.float64)).max(axis=(1, 2))
+        assert (num / den).max() <= parity.X_TOL[dt], f"{what}: L error {(num / den).max()}"
+    Xg, xg = gpu_posv(A_st, B_st, layout, shift)
+    Xo, xo = oracle.posv(A_st, B_st, n, nrhs, layout, shift)
+    np.testing.assert_array_equal(xg, xo, err_msg=f"{what}: posv info")
+    Xg = oracle.rhs_from_storage(Xg, layout, n, nrhs)
+    Xo = oracle.rhs_from_storage(Xo, layout, n, nrhs)
+    assert (Xg[~ok] == 0).all() and not np.signbit(Xg[~ok]).any(), what
+    if ok.any():
+        As = A_l[ok].astype(np.float64) + shift * np.eye(n)
+        As = As.astype(dt)
+        kap = metrics.kappa_inf(As)
+        err = metrics.normwise_error(Xg[ok], Xo[ok])
+        good = kap <= parity.KAPPA_MAX
+        if good.any():
+            assert err[good].max() <= parity.X_TOL[dt], f"{what}: X error {err[good].max()}"
+        res = metrics.residual_ratio(As, Xg[ok], B_l[ok], dt)
+        assert res.max() <= parity.RESID_TOL, f"{what}: residual {res.max()}"
+    return ig
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_exact_integer_factors(dtype, layout):
+    rng = np.random.default_rng(51)
+    for n, nrhs in [(1, 1), (4, 2), (8, 1), (16, 4), (24, 2), (32, 1), (48, 3), (64, 8)]:
+        L = np.tril(rng.integers(-1, 2, (n, n)), -1) + np.diag(rng.choice([1, 2, 4], n))
+        A = (L @ L.T)[None].astype(_np(dtype))
+        x = rng.integers(-3, 4, (1, n, nrhs))
+        b = (A.astype(np.float64) @ x).astype(_np(dtype))
+        Lg, info = gpu_potrf(oracle.to_storage(A, layout), layout)
+        assert info[0] == 0
+        np.testing.assert_array_equal(oracle.from_storage(Lg, layout, n)[0], L.astype(_np(dtype)))
+        X, info = gpu_posv(oracle.to_storage(A, layout), oracle.rhs_to_storage(b, layout), layout)
+        np.testing.assert_array_equal(oracle.rhs_from_storage(X, layout, n, nrhs)[0],
+                                      x[0].astype(_np(dtype)), err_msg=f"n={n}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_every_n_with_failures(dtype, layout):
+    """n = 1..64 (padded kernels included): SPD systems plus, mixed in, one
+    that is not symmetric, one indefinite and one with a zero pivot."""
+    rng = np.random.default_rng(52)
+    for n in range(1, 65):
+        nrhs = int(rng.integers(1, 9))
+        batch = int(rng.integers(5, 40))
+        A = spd(rng, batch, n, _np(dtype))
+        if n > 1:
+            A[1, n - 1, 0] = A[1, n - 1, 0] + 1          # not symmetric -> -2
+            A[2, n - 1, n - 1] = -1                      # indefinite at the last step
+        A[3] = 0                                         # zero matrix -> 1
+        B = rng.standard_normal((batch, n, nrhs)).astype(_np(dtype))
+        info = check(A, B, layout, what=f"{dtype} {layout} n={n}")
+        assert info[3] == 1
+        if n > 1:
+            assert info[1] == -2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_shift(dtype):
+    rng = np.random.default_rng(53)
+    for n in (8, 16, 32, 64):
+        A = spd(rng, 70, n, _np(dtype), shift_diag=0.0)   # G G^T / n: often nearly singular
+        B = rng.standard_normal((70, n, 2)).astype(_np(dtype))
+        check(A, B, "row", shift=0.75, what=f"shift n={n}")
+        info = check(A, B, "col", shift=-50.0, what=f"negative shift n={n}")
+        assert (info > 0).all()
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SPD_RECIPES))
+def test_spd_recipes_small(name):
+    r = workloads.SPD_RECIPES[name]
+    spb = tdls.plan_op("posv", r.dtype, r.layout, r.n, r.nrhs, 1)["systems_per_block"]
+    w = workloads.make(name, seed=0, batch=23 * spb + 7)
+    A = oracle.from_storage(w.A, w.layout, w.n)
+    B = oracle.rhs_from_storage(w.B, w.layout, w.n, w.nrhs)
+    info = check(np.ascontiguousarray(A), np.ascontiguousarray(B), w.layout, what=name)
+    assert (info == 0).all()
+
+
+def test_spd_full_size_sampled():
+    w = workloads.make("spd_n32_f64_col", seed=0)
+    X, info = gpu_posv(w.A, w.B, w.layout)
+    assert (info == 0).all()
+    rng = np.random.default_rng(54)
+    idx = np.unique(np.concatenate([[0, w.batch - 1], rng.choice(w.batch, 2000, replace=False)]))
+    Xo, io = oracle.posv(np.ascontiguousarray(w.A[idx]), np.ascontiguousarray(w.B[idx]), w.n,
+                         w.nrhs, w.layout)
+    Xg = oracle.rhs_from_storage(X[idx], w.layout, w.n, w.nrhs)
+    Xo = oracle.rhs_from_storage(Xo, w.layout, w.n, w.nrhs)
+    err = metrics.normwise_error(Xg, Xo)
+    assert err.max() <= parity.X_TOL[np.dtype(np.float64)]
+
+
+def test_group_size_does_not_change_results(monkeypatch):
+    rng = np.random.default_rng(55)
+    compared = 0
+    for dtype in ("f32", "f64"):
+        for n, nrhs in ((8, 1), (16, 4), (24, 2), (32, 1)):
+            code = tdls.F64 if dtype == "f64" else tdls.F32
+            sizes = []
+            for t in (4, 16, 32, 64):
+                monkeypatch.setenv("TDLS_GROUP_SIZE", str(t))
+                if tdls.tdls_plan_op(tdls.OP_POSV, code, tdls.ROW_MAJOR, n, nrhs, 1)[0] == 0 and \
+                        tdls.tdls_plan_op(tdls.OP_POTRF, code, tdls.ROW_MAJOR, n, 1, 1)[0] == 0:
+                    sizes.append(t)
+            monkeypatch.delenv("TDLS_GROUP_SIZE")
+            if len(sizes) < 2:
+                continue
+            A = spd(rng, 157, n, _np(dtype))
+            B = rng.standard_normal((157, n, nrhs)).astype(_np(dtype))
+            out = []
+            for t in sizes:
+                monkeypatch.setenv("TDLS_GROUP_SIZE", str(t))
+                out.append(gpu_potrf(A, "row") + gpu_posv(A, B, "row"))
+            monkeypatch.delenv("TDLS_GROUP_SIZE")
+            for t, o in zip(sizes[1:], out[1:]):
+                for u, v in zip(out[0], o):
+                    np.testing.assert_array_equal(u, v, err_msg=f"{dtype} n={n} T={t}")
+            compared += 1
+    assert compared > 0
+
+
+def test_contract_and_errors():
+    rng = np.random.default_rng(56)
+    A = torch.from_numpy(spd(rng, 300, 32, np.float64)).to(DEV)
+    B = torch.from_numpy(rng.standard_normal((300, 32, 2))).to(DEV)
+    A0, B0 = A.clone(), B.clone()
+    L = torch.full_like(A, float("nan"))
+    info = torch.full((300,), -7, dtype=torch.int32, device=DEV)
+    tdls.potrf_batched(A, "row", out=(L, info))
+    X = torch.full_like(B, float("nan"))
+    info2 = torch.full((300,), -7, dtype=torch.int32, device=DEV)
+    tdls.posv_batched(A, B, "row", out=(X, info2))
+    torch.cuda.synchronize()
+    assert torch.equal(A, A0) and torch.equal(B, B0)
+    assert torch.isfinite(L).all() and torch.isfinite(X).all()
+    assert (info == 0).all() and (info2 == 0).all()
+    E = torch.zeros((0, 8, 8), device=DEV)
+    Le, ie = tdls.potrf_batched(E, "row")
+    assert Le.shape == (0, 8, 8) and ie.shape == (0,)
+    s = torch.cuda.current_stream().cuda_stream
+    assert tdls.tdls_potrf_batched(tdls.F64, tdls.ROW_MAJOR, 32, 300, float("inf"), A.data_ptr(),
+                                   L.data_ptr(), info.data_ptr(), s) == -5
+    assert tdls.tdls_potrf_batched(tdls.F64, tdls.ROW_MAJOR, 32, 300, 0.0, A.data_ptr(),
+                                   A.data_ptr(), info.data_ptr(), s) == -7
+    assert tdls.tdls_posv_batched(tdls.F64, tdls.ROW_MAJOR, 32, 2, 300, float("nan"),
+                                  A.data_ptr(), B.data_ptr(), X.data_ptr(), info.data_ptr(),
+                                  s) == -6
+    assert tdls.tdls_posv_batched(tdls.F64, tdls.ROW_MAJOR, 32, 2, 300, 0.0, A.data_ptr(),
+                                  B.data_ptr(), B.data_ptr(), info.data_ptr(), s) == -9
+    torch.cuda.synchronize()
