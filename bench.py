@@ -45,6 +45,10 @@ def algorithmic_bytes(n: int, nrhs: int, es: int, op: str = "gesv") -> int:
         return 2 * n * n * es + 4 * n + 4
     if op == "getrs":
         return n * n * es + 4 * n + 2 * n * nrhs * es
+    if op == "potrf":                    # A read, L written, info
+        return 2 * n * n * es + 4
+    if op == "posv":                     # A, B read, X, info written
+        return n * n * es + 2 * n * nrhs * es + 4
     return n * n * es + 2 * n * nrhs * es + 4 * n + 4
 
 
@@ -57,7 +61,11 @@ def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
     s1 = sum(range(1, n))
     elim = 2 * s2 + s1
     subst = nrhs * (2 * n * (n - 1) + n)
-    return {"getrf": elim, "getrs": subst}.get(op, elim + subst)
+    # Cholesky: column j costs j multiply-adds for the diagonal, (n-1-j)*j
+    # for the entries below it, one square root and n-1-j divisions
+    chol = sum(2 * j + 1 + (n - 1 - j) * (2 * j + 1) for j in range(n))
+    return {"getrf": elim, "getrs": subst, "potrf": chol,
+            "posv": chol + subst}.get(op, elim + subst)
 
 
 def kernel_source_hash() -> str:
@@ -156,6 +164,10 @@ def cpu_baseline(w, op: str = "gesv", min_seconds: float = 10.0,
     def run(cnt):
         if op == "getrf":
             oracle.getrf(A[:cnt], n, layout, nthreads=cores)
+        elif op == "potrf":
+            oracle.potrf(A[:cnt], n, layout, nthreads=cores)
+        elif op == "posv":
+            oracle.posv(A[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
         elif op == "getrs":
             oracle.getrs(LU[:cnt], ipiv[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
         else:
@@ -185,9 +197,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--op", default="gesv", choices=["gesv", "getrf", "getrs"],
-                    help="gesv (default: factor and solve in one call), getrf (factor only) "
-                         "or getrs (solve from factors made, untimed, by getrf)")
+    ap.add_argument("--op", default="gesv", choices=["gesv", "getrf", "getrs", "potrf", "posv"],
+                    help="gesv (default: factor and solve in one call), getrf (factor only), "
+                         "getrs (solve from factors made, untimed, by getrf), or the Cholesky "
+                         "potrf / posv (on an spd_* workload)")
     ap.add_argument("--batch", type=int, default=0, help="override the recipe's batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -236,10 +249,15 @@ def main():
     elif op == "getrf":
         LU = torch.empty_like(A)
         step = lambda: tdls.getrf_batched(A, w.layout, out=(LU, piv, info))
-    else:
+    elif op == "getrs":
         LU = torch.empty_like(A)
         tdls.getrf_batched(A, w.layout, out=(LU, piv, info))     # factors, untimed
         step = lambda: tdls.getrs_batched(LU, piv, B, w.layout, out=X)
+    elif op == "potrf":
+        Lc = torch.empty_like(A)
+        step = lambda: tdls.potrf_batched(A, w.layout, out=(Lc, info))
+    else:
+        step = lambda: tdls.posv_batched(A, B, w.layout, out=(X, info))
 
     for _ in range(args.warmup):
         step()
@@ -262,6 +280,9 @@ def main():
     # sample (for getrf: the solve of the timed factors)
     if op == "getrf":
         tdls.getrs_batched(LU, piv, B, w.layout, out=X)
+        torch.cuda.synchronize()
+    if op == "potrf":
+        tdls.posv_batched(A, B, w.layout, out=(X, info))
         torch.cuda.synchronize()
     info_h = info.cpu().numpy()
     rng = np.random.default_rng(0)

@@ -42,9 +42,13 @@ struct CholShape {
   static constexpr int R = (N + T - 1) / T;
   static constexpr int G = kWaveSize / T;
   static constexpr int SL = T < 16 ? T : 16;
-  static constexpr int S = N + 1;   // LDS row stride (odd: no bank conflicts)
+  static constexpr int S = N + 1;   // LDS row stride of the symmetry chunks (odd)
+  static constexpr int CH = T < 16 ? T : 16;   // rows per symmetry chunk (within one slot)
   static constexpr int VEC = RealTraits<Real>::VEC;
-  static constexpr int GROUP_ELEMS = (N * S + VEC - 1) / VEC * VEC;
+  static constexpr int UTRI_PAD = (N * (N + 1) / 2 + VEC - 1) / VEC * VEC;
+  static constexpr int BIG1 = CH * S > UTRI_PAD ? CH * S : UTRI_PAD;
+  static constexpr int BIG2 = BIG1 > N * NRHS ? BIG1 : N * NRHS;
+  static constexpr int GROUP_ELEMS = (BIG2 + VEC - 1) / VEC * VEC;
   static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
   static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
 };
@@ -162,31 +166,39 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
   }
 
-  // ---- exact symmetry: every row is written to LDS, lane tx compares its
-  // row q with column q read back
-  bool asym = false;
-  sfor<0, R>([&](auto Kc) {
-    constexpr int K = decltype(Kc)::value;
-    const int q = tx + K * T;
-    if (q < N) {
-      sfor<0, N>([&](auto cc) { sq[q * ST + decltype(cc)::value] = a[K][decltype(cc)::value]; });
+  // ---- exact symmetry: CH rows at a time (lanes of one slot) go to LDS,
+  // and every lane compares its row q with column q of the chunk
+  int asym = 0;   // a lane value, settled per chunk (see below)
+  sfor<0, (N + S::CH - 1) / S::CH>([&](auto cic) {
+    constexpr int r0 = decltype(cic)::value * S::CH;
+    constexpr int KC = r0 / T;                  // the slot holding rows r0 .. r0+CH-1
+    constexpr int t0 = r0 - KC * T;             // and the first lane
+    if (tx >= t0 && tx < t0 + S::CH && tx + KC * T < N) {
+      sfor<0, N>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        sq[(tx - t0) * ST + c] = a[KC][c];
+      });
     }
-  });
-  wave_sync_lds();
-  sfor<0, R>([&](auto Kc) {
-    constexpr int K = decltype(Kc)::value;
-    const int q = tx + K * T;
-    const int qq = q < N ? q : N - 1;
-    sfor<0, N>([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      asym = asym | ((q < N) & !(sq[c * ST + qq] == a[K][c]));   // phantom rows excluded
+    wave_sync_lds();
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      const int qq = q < N ? q : N - 1;
+      sfor<0, S::CH>([&](auto rc) {
+        constexpr int r = r0 + decltype(rc)::value;
+        if constexpr (r < N)
+          asym |= (int)((q < N) & !(sq[(r - r0) * ST + qq] == a[K][r]));   // phantom rows excluded
+      });
     });
+    // settled now: left to the end, every comparison's lane mask stays live
+    // in scalar registers
+    asm volatile("" : "+v"(asym));
+    wave_sync_lds();   // the chunk is rewritten next
   });
-  wave_sync_lds();   // the copy is rewritten below
   int status;
   {
     // one status per group: any lane of the group that saw a mismatch
-    const uint64_t m = __builtin_amdgcn_ballot_w64(asym);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(asym != 0);
     uint64_t gm;
     if constexpr (T == 64)
       gm = m;
@@ -237,10 +249,11 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         asm volatile("" : "+v"(a[K][j]));
       }
     });
-    // forward substitution: y_j / d on its lane, then y_j leaves the rows below
+    // forward substitution (one right-hand side: folded into the steps):
+    // y_j / d on its lane, then y_j leaves the rows below
     sfor<0, NRHS>([&](auto rc) {
       constexpr int r = decltype(rc)::value;
-      if constexpr (!FACT) {
+      if constexpr (!FACT && NRHS == 1) {
         const Real yj = y[js][r] / d;
         y[js][r] = tx == jl ? yj : y[js][r];
         const Real yb = group_bcast<T, BL>(y[js][r]);
@@ -266,6 +279,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
                                                                         lm[K]);
         });
       } else {
+        // a few readlanes at a time: hoisted all together they fill the
+        // scalar registers
+        if constexpr (c % 8 == 0) __builtin_amdgcn_sched_barrier(0);
         const Real lc = group_bcast<T, cl>(a[cs][j]);
         sfor<cs, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
@@ -312,63 +328,162 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       if (tx == 0) info[sys] = status;
     }
   } else {
-    // ---- L^T x = y: L by rows into LDS, then x_j = y_j / L(j,j) on its
-    // lane, removed from the rows above with L(j,q) read at row j, column q
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      if (q < N) {
-        sfor<0, N>([&](auto cc) { sq[q * ST + decltype(cc)::value] = a[K][decltype(cc)::value]; });
-      }
-    });
-    wave_sync_lds();
-    Real xr[R][NRHS];
-    sfor<0, R>([&](auto Kc) {
-      sfor<0, NRHS>([&](auto rc) { xr[decltype(Kc)::value][decltype(rc)::value] = Real(0); });
-    });
-    sfor<0, N>([&](auto ic) {
-      constexpr int j = N - 1 - decltype(ic)::value;
-      constexpr int js = j / T;
-      constexpr int jl = j % T;
-      __builtin_amdgcn_sched_barrier(0);
-      Real lj[js + 1];
-      sfor<0, js + 1>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        const int q = tx + K * T;
-        lj[K] = sq[j * ST + (q < N ? q : N - 1)];   // L(j, q), meaningful for q < j
-      });
-      const Real djj = a[js][j];
-      sfor<0, NRHS>([&](auto rc) {
-        constexpr int r = decltype(rc)::value;
-        const Real x = y[js][r] / djj;   // meaningful on lane jl
-        xr[js][r] = tx == jl ? x : xr[js][r];
-        asm volatile("" : "+v"(xr[js][r]));
-        constexpr int BL = T == 64 ? jl : jl % SL;
-        const Real xb = group_bcast<T, BL>(x);
-        sfor<0, js + 1>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          y[K][r] = __builtin_fma(-lj[K], xb, y[K][r]);
-        });
-      });
-    });
-    if (live) {
-      Real* Xs = X + sys * ((int64_t)n * nrhs);
+    if constexpr (NRHS == 1) {
+      // ---- L^T x = y with the solver of the LU path: U = L^T, so lane c
+      // writes L(c, q) into row q of the triangular store for every q <= c
+      upper_solve_store<Real, N, NRHS, T>(
+          sq, tx, (int)(g * T), live, failed, live ? sys : 0, n, nrhs, col, X,
+          [&](Real* yt) {
+            sfor<0, R>([&](auto Kc) {
+              constexpr int K = decltype(Kc)::value;
+              const int q = tx + K * T;
+              if (q < N) yt[q] = y[K][0];
+            });
+          },
+          [&](Real* ut) {
+            sfor<0, R>([&](auto Kc) {
+              constexpr int K = decltype(Kc)::value;
+              const int c = tx + K * T;
+              if (c < N) {
+                Real* colp = ut + c;
+                sfor<0, (K + 1) * T < N ? (K + 1) * T : N>([&](auto qc) {
+                  constexpr int q = decltype(qc)::value;
+                  if (q <= c) colp[utri_row<N>(q) - q] = a[K][q];
+                });
+              }
+            });
+          });
+    } else {
+      // ---- several right-hand sides: both triangular solves run after the
+      // factorization in the column-class / row-phase layout of the LU
+      // path, one division per column class per step, L read from a
+      // row-packed lower triangle in LDS (row i at i (i + 1) / 2).
+      constexpr int NJ = NRHS < T ? NRHS : T;
+      constexpr int P = T / NJ;
+      constexpr int JR = NRHS / NJ;
+      constexpr int QR = (N + P - 1) / P;
+      const int j0 = tx % NJ;
+      const int ph = tx / NJ;
+      const int gb = g * T;
+      auto ltri = [](int i) { return i * (i + 1) / 2; };
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
-        if (q < n) {
+        if (q < N) {
           sfor<0, NRHS>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            if (r < nrhs) {
-              const Real v = failed ? Real(0) : xr[K][r];
+            sq[q * NRHS + r] = y[K][r];
+          });
+        }
+      });
+      wave_sync_lds();
+      Real yv[QR][JR], xr[QR][JR];
+      const Real* lrow[QR];
+      sfor<0, QR>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const int q = ph + P * m;
+        const int qq = q < N ? q : N - 1;
+        sfor<0, JR>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          yv[m][jj] = sq[qq * NRHS + j0 + NJ * jj];
+          xr[m][jj] = Real(0);
+        });
+        lrow[m] = sq + ltri(qq);   // L(q, c) at lrow[m][c], c <= q
+      });
+      wave_sync_lds();   // right-hand sides read before L overwrites them
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        if (q < N) {
+          Real* rowp = sq + ltri(q);
+          sfor<0, (K + 1) * T < N ? (K + 1) * T : N>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if (c <= q) rowp[c] = a[K][c];
+          });
+        }
+      });
+      wave_sync_lds();
+      // L y = b: y_k / L(k,k) on the lanes of phase k % P, then y_k leaves
+      // the rows below it (rows at or above k are final and keep their value)
+      sfor<0, N>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int kp = k % P;
+        constexpr int km = k / P;
+        __builtin_amdgcn_sched_barrier(0);
+        const Real lkk = lrow[km][k];   // L(k,k) on the lanes of phase kp
+        Real lik[QR];
+        sfor<km, QR>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          const Real v = lrow[m][k];    // L(i,k), i = ph + P*m (meaningful for i > k)
+          if constexpr (m == km)
+            lik[m] = ph > kp ? v : Real(0);
+          else
+            lik[m] = v;
+        });
+        sfor<0, JR>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          const Real yk = yv[km][jj] / lkk;
+          yv[km][jj] = ph == kp ? yk : yv[km][jj];
+          Real yb;
+          if constexpr (P == 1)
+            yb = yk;
+          else
+            yb = lane_fetch_any(yk, gb + kp * NJ + j0);
+          sfor<km, QR>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            yv[m][jj] = __builtin_fma(-lik[m], yb, yv[m][jj]);
+          });
+        });
+      });
+      // L^T x = y: x_k = y_k / L(k,k) on the lanes of phase k % P, removed
+      // from the rows above with L(k, q) (rows at or below k are done)
+      sfor<0, N>([&](auto ic) {
+        constexpr int k = N - 1 - decltype(ic)::value;
+        constexpr int kp = k % P;
+        constexpr int km = k / P;
+        __builtin_amdgcn_sched_barrier(0);
+        const Real lkk = lrow[km][k];
+        Real lkq[km + 1];
+        sfor<0, km + 1>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          lkq[m] = sq[ltri(k) + (ph + P * m < N ? ph + P * m : N - 1)];   // L(k, q)
+        });
+        sfor<0, JR>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          const Real x = yv[km][jj] / lkk;   // meaningful on the lanes of phase kp
+          xr[km][jj] = ph == kp ? x : xr[km][jj];
+          asm volatile("" : "+v"(xr[km][jj]));
+          Real xb;
+          if constexpr (P == 1)
+            xb = x;
+          else
+            xb = lane_fetch_any(x, gb + kp * NJ + j0);
+          sfor<0, km + 1>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            yv[m][jj] = __builtin_fma(-lkq[m], xb, yv[m][jj]);
+          });
+        });
+      });
+      if (live) {
+        Real* Xs = X + sys * ((int64_t)n * nrhs);
+        sfor<0, QR>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          const int q = ph + P * m;
+          sfor<0, JR>([&](auto jc) {
+            constexpr int jj = decltype(jc)::value;
+            const int r = j0 + NJ * jj;
+            if (q < n && r < nrhs) {
+              const Real v = failed ? Real(0) : xr[m][jj];
               if (col)
                 Xs[(int64_t)r * n + q] = v;
               else
                 Xs[(int64_t)q * nrhs + r] = v;
             }
           });
-        }
-      });
+        });
+      }
+    }
+    if (live) {
       if (tx == 0) info[sys] = status;
     }
   }

@@ -59,7 +59,7 @@ static int launch_chol(const LaunchPlan& p, const void* A, const void* B, void* 
     return (int)hipErrorInvalidConfiguration;   // no Cholesky kernel for 32-lane groups
   } else {
     using S = CholShape<Real, N, NRHS, T>;
-    static_assert(S::BLOCK_BYTES == chol_lds_bytes(N, T, sizeof(Real) == 8),
+    static_assert(S::BLOCK_BYTES == chol_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
                   "host and device LDS sizes disagree");
     static_assert(S::BLOCK_BYTES <= 65536, "Cholesky LDS stays within the default limit");
     if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;

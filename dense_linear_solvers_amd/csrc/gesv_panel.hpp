@@ -242,6 +242,172 @@ __device__ __forceinline__ uint32_t lo_word(double v) {
 
 // ------------------------------------------------------------- kernel
 
+// ---- back substitution shared by the LU and Cholesky kernels
+//
+// Row q of the packed upper-triangular store (columns q..N-1) starts at
+// utri_row(q).
+template <int N>
+__device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2; }
+
+// U x = y for the group's system, then X stored (all +0.0 when `failed`).
+// `ut` is the group's LDS area (at least max(N * NRHS, N (N + 1) / 2)
+// entries).  write_rhs(ut) must store the right-hand sides by position
+// (entry (q, j) at ut[q * NRHS + j]); write_u(ut) must then store row q of U
+// at ut + utri_row(q) - q + c for columns c >= q, over them.
+//
+// x_k = y_k / U(k,k) by IEEE division for k = n-1 .. 0, each x_k removed from
+// the rows above by fused multiply-adds (the order of the TDLS page's
+// Detailed Description, the solution entry kept by its owner).  One
+// right-hand side: lane tx holds the positions tx + K*T, x_k is formed on
+// lane k % T and reaches the rows above by DPP inside the FMA (a lane fetch
+// for groups wider than a 16-lane row).  Several: the group's lanes split
+// into NJ column classes and P row phases; lane (ph, j0) holds the columns
+// j = j0 + NJ*jj of the positions ph + P*m, so x_k costs one division per
+// column class on the lanes of phase k % P, handed to the lanes of the same
+// class by a lane fetch; U(q, k) is read from the store.
+template <typename Real, int N, int NRHS, int T, typename WR, typename WU>
+__device__ __forceinline__ void upper_solve_store(Real* ut, int tx, int gbase, bool live,
+                                                  bool failed, int64_t sys, int n, int nrhs,
+                                                  int col, Real* X, WR&& write_rhs,
+                                                  WU&& write_u) {
+  constexpr int R = (N + T - 1) / T;
+  write_rhs(ut);
+  wave_sync_lds();
+  Real* Xs = X + sys * ((int64_t)n * nrhs);
+  // layout of the solve (see below): one right-hand side by slots; several
+  // by column classes and row phases
+  constexpr int NJ = NRHS < T ? NRHS : T;
+  constexpr int P = NRHS == 1 ? T : T / NJ;
+  constexpr int JR = NRHS / NJ;
+  constexpr int QR = (N + P - 1) / P;
+  const int j0 = NRHS == 1 ? 0 : tx % NJ;
+  const int ph = NRHS == 1 ? tx : tx / NJ;
+  Real yv[QR][JR];
+  sfor<0, QR>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    const int q = ph + P * m;
+    const int qq = q < N ? q : N - 1;
+    sfor<0, JR>([&](auto jc) {
+      constexpr int jj = decltype(jc)::value;
+      yv[m][jj] = ut[qq * NRHS + j0 + NJ * jj];
+    });
+  });
+  wave_sync_lds();  // read before U overwrites them
+  write_u(ut);
+  wave_sync_lds();
+  const Real* rw[QR];
+  sfor<0, QR>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    const int q = ph + P * m;
+    const int qq = q < N ? q : N - 1;
+    rw[m] = ut + utri_row<N>(qq) - qq;   // entry of column c at rw[m][c]
+  });
+
+  if constexpr (NRHS == 1) {
+    // One right-hand side: lane tx holds the positions tx + K*T; x_k is
+    // formed by lane k % T (slot k / T) and reaches the rows above by DPP
+    // inside the FMA (a lane fetch for groups wider than a 16-lane row).
+    // x of the positions tx + K*T, kept by this lane until the final store
+    // (every entry is assigned at its own step)
+    Real xr[R];
+    sfor<0, R>([&](auto Kc) { xr[decltype(Kc)::value] = Real(0); });
+    sfor<0, N>([&](auto ic) {
+      constexpr int k = N - 1 - decltype(ic)::value;
+      constexpr int kl = k % T;
+      constexpr int ks = k / T;
+      constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
+      // keep the U reads of one step together with their use (hoisting them
+      // all ahead of the loop costs registers, not latency)
+      __builtin_amdgcn_sched_barrier(0);
+      Real uk[ks + 1];
+      sfor<0, ks + 1>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        uk[K] = rw[K][k];   // u(q, k) of this lane's row q in slot K
+      });
+      const Real x = yv[ks][0] / uk[ks];   // meaningful on lane kl
+      xr[ks] = tx == kl ? x : xr[ks];
+      asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
+      // rows above k take x_k (rows at k and below are done: their updates
+      // are never read)
+      if constexpr (T <= 16) {
+        sfor<0, ks + 1>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          fnmac_bcast<T, SLK, K == 0>(yv[K][0], x, uk[K]);
+        });
+      } else {
+        const Real xk = lane_fetch<T>(x, gbase + kl);
+        sfor<0, ks + 1>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          yv[K][0] = __builtin_fma(-uk[K], xk, yv[K][0]);
+        });
+      }
+    });
+    if (live) {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        if (q < n) Xs[q] = failed ? Real(0) : xr[K];   // one column: same address in both layouts
+      });
+    }
+  } else {
+    // Several right-hand sides: the group's lanes split into NJ column
+    // classes and P row phases.  Lane (ph, j0) holds the right-hand-side
+    // columns j = j0 + NJ*jj of the positions q = ph + P*m, so each x_k is
+    // one division per column on the NJ lanes of phase k % P, handed to the
+    // lanes of the same column class by a lane fetch; every lane then folds
+    // it into its rows, reading u(q, k) from the triangular store.
+    Real xr[QR][JR];
+    sfor<0, QR>([&](auto mc) {
+      sfor<0, JR>([&](auto jc) { xr[decltype(mc)::value][decltype(jc)::value] = Real(0); });
+    });
+    sfor<0, N>([&](auto ic) {
+      constexpr int k = N - 1 - decltype(ic)::value;
+      constexpr int kp = k % P;
+      constexpr int km = k / P;
+      __builtin_amdgcn_sched_barrier(0);
+      Real uk[km + 1];
+      sfor<0, km + 1>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        uk[m] = rw[m][k];   // u(q, k) of row q = ph + P*m (meaningful for q <= k)
+      });
+      const int src = gbase + kp * NJ + j0;   // the lane of phase kp, same column class
+      sfor<0, JR>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        const Real x = yv[km][jj] / uk[km];   // meaningful on the lanes of phase kp
+        xr[km][jj] = ph == kp ? x : xr[km][jj];
+        asm volatile("" : "+v"(xr[km][jj]));
+        Real xk;
+        if constexpr (P == 1)
+          xk = x;   // every lane is the owner of its own column class
+        else
+          xk = lane_fetch_any(x, src);
+        sfor<0, km + 1>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          yv[m][jj] = __builtin_fma(-uk[m], xk, yv[m][jj]);
+        });
+      });
+    });
+    if (live) {
+      sfor<0, QR>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const int q = ph + P * m;
+        sfor<0, JR>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          const int j = j0 + NJ * jj;
+          if (q < n && j < nrhs) {
+            const Real v = failed ? Real(0) : xr[m][jj];
+            if (col)
+              Xs[(int64_t)j * n + q] = v;
+            else
+              Xs[(int64_t)q * nrhs + j] = v;
+          }
+        });
+      });
+    }
+  }
+
+}
+
 // FACT = false: gesv, X receives the solutions.  FACT = true: getrf (NRHS
 // must be 1 and Bm is not read), X receives the factors in the layout of A:
 // LAPACK's row order, unit-lower L below the diagonal and U on and above it.
@@ -645,169 +811,39 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
   } else {
 
-  // ---- back substitution.  Every row, whatever lane holds it, writes its
-  // right-hand sides to the store at its position; the lanes read them back
-  // in the layout of the solve below; then every row writes its U entries
-  // (columns from its position on) over them, into the packed triangular
-  // store, which the solve reads by position.
-  auto urow = [](int q) { return q * N - q * (q - 1) / 2; };   // row q offset
-  wave_sync_lds();  // the last records have been read
-  Real* ut = rec;   // the group's LDS area
-  sfor<0, R>([&](auto Kc) {
-    constexpr int K = decltype(Kc)::value;
-    const int q = lab[K];
-    if (q >= 0) {
-      sfor<0, NRHS>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        ut[q * NRHS + j] = y[K][j];
-      });
-    }
-  });
-  wave_sync_lds();
+  // ---- back substitution (see upper_solve_store): every row, whatever lane
+  // holds it, stores its right-hand sides and then its U entries (columns
+  // from its position on) by position
   const bool failed = status != 0;
   int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
-  Real* Xs = X + (live ? sys : 0) * ((int64_t)n * nrhs);
-  // layout of the solve (see below): one right-hand side by slots; several
-  // by column classes and row phases
-  constexpr int NJ = NRHS < T ? NRHS : T;
-  constexpr int P = NRHS == 1 ? T : T / NJ;
-  constexpr int JR = NRHS / NJ;
-  constexpr int QR = (N + P - 1) / P;
-  const int j0 = NRHS == 1 ? 0 : tx % NJ;
-  const int ph = NRHS == 1 ? tx : tx / NJ;
-  Real yv[QR][JR];
-  sfor<0, QR>([&](auto mc) {
-    constexpr int m = decltype(mc)::value;
-    const int q = ph + P * m;
-    const int qq = q < N ? q : N - 1;
-    sfor<0, JR>([&](auto jc) {
-      constexpr int jj = decltype(jc)::value;
-      yv[m][jj] = ut[qq * NRHS + j0 + NJ * jj];
-    });
-  });
-  wave_sync_lds();  // read before U overwrites them
-  sfor<0, R>([&](auto Kc) {
-    constexpr int K = decltype(Kc)::value;
-    const int q = lab[K];
-    if (q >= 0) {
-      Real* row = ut + urow(q) - q;   // entry of column c at row[c]
-      sfor<0, N>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        if (c >= q) row[c] = a[K][c];
-      });
-    }
-  });
-  wave_sync_lds();
-  const Real* rw[QR];
-  sfor<0, QR>([&](auto mc) {
-    constexpr int m = decltype(mc)::value;
-    const int q = ph + P * m;
-    const int qq = q < N ? q : N - 1;
-    rw[m] = ut + urow(qq) - qq;   // entry of column c at rw[m][c]
-  });
-
-  if constexpr (NRHS == 1) {
-    // One right-hand side: lane tx holds the positions tx + K*T; x_k is
-    // formed by lane k % T (slot k / T) and reaches the rows above by DPP
-    // inside the FMA (a lane fetch for groups wider than a 16-lane row).
-    // x of the positions tx + K*T, kept by this lane until the final store
-    // (every entry is assigned at its own step)
-    Real xr[R];
-    sfor<0, R>([&](auto Kc) { xr[decltype(Kc)::value] = Real(0); });
-    sfor<0, N>([&](auto ic) {
-      constexpr int k = N - 1 - decltype(ic)::value;
-      constexpr int kl = k % T;
-      constexpr int ks = k / T;
-      constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
-      // keep the U reads of one step together with their use (hoisting them
-      // all ahead of the loop costs registers, not latency)
-      __builtin_amdgcn_sched_barrier(0);
-      Real uk[ks + 1];
-      sfor<0, ks + 1>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        uk[K] = rw[K][k];   // u(q, k) of this lane's row q in slot K
-      });
-      const Real x = yv[ks][0] / uk[ks];   // meaningful on lane kl
-      xr[ks] = tx == kl ? x : xr[ks];
-      asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
-      // rows above k take x_k (rows at k and below are done: their updates
-      // are never read)
-      if constexpr (T <= 16) {
-        sfor<0, ks + 1>([&](auto Kc) {
+  wave_sync_lds();  // the last records have been read
+  upper_solve_store<Real, N, NRHS, T>(
+      rec, tx, gbase, live, failed, live ? sys : 0, n, nrhs, col, X,
+      [&](Real* yt) {
+        sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          fnmac_bcast<T, SLK, K == 0>(yv[K][0], x, uk[K]);
+          const int q = lab[K];
+          if (q >= 0) {
+            sfor<0, NRHS>([&](auto jc) {
+              constexpr int j = decltype(jc)::value;
+              yt[q * NRHS + j] = y[K][j];
+            });
+          }
         });
-      } else {
-        const Real xk = lane_fetch<T>(x, gbase + kl);
-        sfor<0, ks + 1>([&](auto Kc) {
+      },
+      [&](Real* ut) {
+        sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          yv[K][0] = __builtin_fma(-uk[K], xk, yv[K][0]);
-        });
-      }
-    });
-    if (live) {
-      sfor<0, R>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        const int q = tx + K * T;
-        if (q < n) Xs[q] = failed ? Real(0) : xr[K];   // one column: same address in both layouts
-      });
-    }
-  } else {
-    // Several right-hand sides: the group's lanes split into NJ column
-    // classes and P row phases.  Lane (ph, j0) holds the right-hand-side
-    // columns j = j0 + NJ*jj of the positions q = ph + P*m, so each x_k is
-    // one division per column on the NJ lanes of phase k % P, handed to the
-    // lanes of the same column class by a lane fetch; every lane then folds
-    // it into its rows, reading u(q, k) from the triangular store.
-    Real xr[QR][JR];
-    sfor<0, QR>([&](auto mc) {
-      sfor<0, JR>([&](auto jc) { xr[decltype(mc)::value][decltype(jc)::value] = Real(0); });
-    });
-    sfor<0, N>([&](auto ic) {
-      constexpr int k = N - 1 - decltype(ic)::value;
-      constexpr int kp = k % P;
-      constexpr int km = k / P;
-      __builtin_amdgcn_sched_barrier(0);
-      Real uk[km + 1];
-      sfor<0, km + 1>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        uk[m] = rw[m][k];   // u(q, k) of row q = ph + P*m (meaningful for q <= k)
-      });
-      const int src = gbase + kp * NJ + j0;   // the lane of phase kp, same column class
-      sfor<0, JR>([&](auto jc) {
-        constexpr int jj = decltype(jc)::value;
-        const Real x = yv[km][jj] / uk[km];   // meaningful on the lanes of phase kp
-        xr[km][jj] = ph == kp ? x : xr[km][jj];
-        asm volatile("" : "+v"(xr[km][jj]));
-        Real xk;
-        if constexpr (P == 1)
-          xk = x;   // every lane is the owner of its own column class
-        else
-          xk = lane_fetch_any(x, src);
-        sfor<0, km + 1>([&](auto mc) {
-          constexpr int m = decltype(mc)::value;
-          yv[m][jj] = __builtin_fma(-uk[m], xk, yv[m][jj]);
-        });
-      });
-    });
-    if (live) {
-      sfor<0, QR>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        const int q = ph + P * m;
-        sfor<0, JR>([&](auto jc) {
-          constexpr int jj = decltype(jc)::value;
-          const int j = j0 + NJ * jj;
-          if (q < n && j < nrhs) {
-            const Real v = failed ? Real(0) : xr[m][jj];
-            if (col)
-              Xs[(int64_t)j * n + q] = v;
-            else
-              Xs[(int64_t)q * nrhs + j] = v;
+          const int q = lab[K];
+          if (q >= 0) {
+            Real* row = ut + utri_row<N>(q) - q;   // entry of column c at row[c]
+            sfor<0, N>([&](auto cc) {
+              constexpr int c = decltype(cc)::value;
+              if (c >= q) row[c] = a[K][c];
+            });
           }
         });
       });
-    }
-  }
 
   // ---- piv (all -1 for a failed system) and info
   if (live) {

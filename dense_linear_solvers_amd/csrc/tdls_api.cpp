@@ -94,7 +94,7 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   if (p->grid > 0x7fffffffLL) return -5;
   p->shift = 0.0;
   p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, T)
-                 : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, T, is64)
+                 : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, NRHS, T, is64)
                                                      : gesv_lds_bytes(N, NRHS, T, is64);
   return 0;
 }

@@ -108,13 +108,18 @@ constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
 // of each group.
 constexpr int getrs_lds_bytes(int N, int T) { return kWavesPerBlock * (kWaveSize / T) * N * 4; }
 
-// LDS bytes of one block (one wave) of the Cholesky kernel: a row-major copy
-// of each group's matrix with an odd row stride (N + 1), rounded up to 16
-// bytes.
-constexpr int chol_lds_bytes(int N, int T, bool is64) {
+// LDS bytes of one block (one wave) of the Cholesky kernel: per group, the
+// largest of a symmetry-check chunk (min(T, 16) rows of stride N + 1), the
+// right-hand sides by position and the packed triangle of the back
+// substitution, rounded up to 16 bytes.
+constexpr int chol_lds_bytes(int N, int NRHS, int T, bool is64) {
   const int es = is64 ? 8 : 4;
   const int vec = 16 / es;
-  return kWavesPerBlock * (kWaveSize / T) * ((N * (N + 1) + vec - 1) / vec * vec) * es;
+  const int ch = T < 16 ? T : 16;
+  const int utri = (N * (N + 1) / 2 + vec - 1) / vec * vec;
+  const int big1 = ch * (N + 1) > utri ? ch * (N + 1) : utri;
+  const int big2 = big1 > N * NRHS ? big1 : N * NRHS;
+  return kWavesPerBlock * (kWaveSize / T) * ((big2 + vec - 1) / vec * vec) * es;
 }
 
 // Launchers, one per shape of TDLS_FOR_EACH_SHAPE, defined in the

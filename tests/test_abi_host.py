@@ -223,5 +223,7 @@ def test_cholesky_validation_before_launch(lib):
     assert s(0.0, a, b, x, x) == -10
     assert tdls.tdls_posv_batched(tdls.F64, tdls.ROW_MAJOR, n, 1, 0, 0.0, 0, 0, 0, 0, 0) == 0
     p = tdls.plan_op("posv", "f64", "col", 32, 1, 1000)
-    assert p["lds_bytes"] == p["systems_per_wave"] * 32 * 33 * 8
+    ch = min(p["group_size"], 16)       # symmetry chunk rows, stride n + 1
+    per_group = max(ch * 33, 32 * 33 // 2, 32 * 1)
+    assert p["lds_bytes"] == p["systems_per_wave"] * per_group * 8
     assert tdls.plan_op("potrf", "f32", "row", 13, 5, 10)["nrhs_kernel"] == 1
