@@ -13,10 +13,12 @@ object prices the kernel's algorithmic HBM bytes per launch against 8 TB/s;
 ``cpu_baseline`` is the plain CPU oracle timed on this host's cores on the
 same inputs.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--op gesv|getrf|getrs] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+                  [--op gesv|getrf|getrs|potrf|posv] [--no-cpu]
   python bench.py --calibrate-copy      # a plain 1 GiB device copy, for
                                         # scaling the HBM byte counters
-  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+  python bench.py [--workload NAME] [--op OP] --summarize-counters \
+                  FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 """
 from __future__ import annotations
 
@@ -24,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -68,20 +71,37 @@ def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
             "posv": chol + subst}.get(op, elim + subst)
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and blank lines (so that a comment edit
+    does not mark the counters as stale)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_linear_solvers_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, launches_per_profile: int = 1):
+# the kernel each op launches (rocprofv3 -T truncates names to these)
+KERNEL_OF_OP = {"gesv": "gesv_panel_kernel", "getrf": "gesv_panel_kernel",
+                "getrs": "getrs_kernel", "potrf": "chol_kernel", "posv": "chol_kernel"}
+
+
+def traffic_path(workload: str, op: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{op}_{workload}_traffic.json")
+
+
+def measured_traffic(workload: str, op: str = "gesv"):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"gesv_{workload}_traffic.json")
+    path = traffic_path(workload, op)
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as fh:
@@ -105,26 +125,29 @@ def _counter_values(csv_dir: str, counter: str, kernel_prefix: str) -> list:
     return vals
 
 
-def summarize_counters(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
-                       copy_write_dir: str, copy_bytes: int = 1 << 30) -> dict:
+def summarize_counters(workload: str, op: str, fetch_dir: str, write_dir: str,
+                       copy_fetch_dir: str, copy_write_dir: str,
+                       copy_bytes: int = 1 << 30) -> dict:
     """HBM bytes per launch of the solver kernel from two rocprofv3 --pmc
     runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
     same counter reads for a plain device copy of ``copy_bytes`` bytes."""
-    fk = float(np.median(_counter_values(fetch_dir, "FETCH_SIZE", "gesv")))
-    wk = float(np.median(_counter_values(write_dir, "WRITE_SIZE", "gesv")))
+    kern = KERNEL_OF_OP[op]
+    fk = float(np.median(_counter_values(fetch_dir, "FETCH_SIZE", kern)))
+    wk = float(np.median(_counter_values(write_dir, "WRITE_SIZE", kern)))
     cf = float(np.median(_counter_values(copy_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")))
     cw = float(np.median(_counter_values(copy_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")))
     fetch_scale = copy_bytes / (cf * 1024.0)
     write_scale = copy_bytes / (cw * 1024.0)
     fetch_b = fk * 1024.0 * fetch_scale
     write_b = wk * 1024.0 * write_scale
-    d = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+    d = {"workload": workload, "op": op, "kernel": kern,
+         "kernel_source_hash": kernel_source_hash(),
          "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
          "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
          "fetch_scale": fetch_scale, "write_scale": write_scale,
          "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
          "hbm_bytes_per_launch": fetch_b + write_b}
-    out = os.path.join(ROOT, "profiles", f"gesv_{workload}_traffic.json")
+    out = traffic_path(workload, op)
     with open(out, "w", encoding="utf-8") as fh:
         json.dump(d, fh, indent=1)
         fh.write("\n")
@@ -206,11 +229,12 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                                                              "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="write profiles/gesv_<workload>_traffic.json from rocprofv3 --pmc "
+                    help="write profiles/<op>_<workload>_traffic.json from rocprofv3 --pmc "
                          "output directories (no GPU needed)")
     args = ap.parse_args()
     if args.summarize_counters:
-        print(json.dumps(summarize_counters(args.workload, *args.summarize_counters), indent=1))
+        print(json.dumps(summarize_counters(args.workload, args.op, *args.summarize_counters),
+                         indent=1))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -330,7 +354,7 @@ def main():
         "vector_frac": achieved_tflops / vec_peak,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name) if op == "gesv" else None},
+                     "traffic": measured_traffic(w.name, op)},
         "check": {"failed_systems": int((info_h != 0).sum()), "residual_max_sample": resid_max},
     }
     if not args.no_cpu:

@@ -27,20 +27,24 @@
 // broadcast from a fixed lane of a 16-lane row rides for free on the fused
 // multiply-add (v_fmac_*_dpp row_newbcast / quad_perm).  The factorization
 // therefore goes by panels of B columns:
-//   * inside a panel, step k updates only column k (with the panel's earlier
-//     pivots, their value fetched from the owning lane by ds_bpermute), finds
-//     the pivot (three DPP max/min passes on the key |a|, then lowest
-//     position), relabels, and forms the multipliers by IEEE division;
+//   * inside a panel, step k searches column k: the largest flagged high word
+//     of |a| (flag = row still at a position >= k) by a DPP max over the
+//     group, a ballot of the slots that hold it, and, when every group of the
+//     wave has exactly one such slot (decided uniformly), that slot wins;
+//     otherwise the low word and then the lowest position decide exactly.
+//     The winning lane hands its key, value and panel entries right of k to
+//     the group in one batch of lane fetches; the rows relabel, form their
+//     multipliers by IEEE division, and the rest of the panel takes the
+//     update at once, so column k+1 is complete when its search starts;
 //   * at the end of the panel, each of its B pivot rows is written once to an
-//     LDS record (trailing columns, right-hand sides, its multipliers inside
-//     the panel); every lane reads back the entries it serves as DPP source
-//     (trailing column t from lane t mod 16), the panel's own updates are
-//     applied to those copies (a small triangular solve), and every row of
-//     the group takes the panel's B rank-1 updates on its trailing columns in
-//     step order, the pivot-row entry broadcast by DPP inside the FMA.
-// Back substitution, k = n-1 .. 0: the owner of position k divides, the
-// quotient reaches the group by ds_bpermute (readlane when T = 64), and the
-// rows above k fold it in.
+//     LDS record (trailing columns and right-hand sides); every lane reads
+//     back the entries it serves as DPP source (trailing column t from lane
+//     t mod 16), and every row of the group takes the panel's B rank-1
+//     updates on its trailing columns in step order, the pivot-row entry
+//     broadcast by DPP inside the FMA.
+// Back substitution (upper_solve_store, shared with the Cholesky kernel):
+// the rows go by position to a packed triangular LDS store, then x_k is
+// formed by the owner of position k and removed from the rows above.
 #pragma once
 
 #include <hip/hip_runtime.h>
