@@ -48,7 +48,7 @@ def _load():
             g = getattr(lib, "oracle_gesv_" + sfx)
             g.restype = ctypes.c_int
             g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
-                          tp, tp, tp, i32p, i32p, ctypes.c_int]
+                          ctypes.c_int, tp, tp, tp, i32p, i32p, ctypes.c_int]
             r = getattr(lib, "oracle_getrs_" + sfx)
             r.restype = ctypes.c_int
             r.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
@@ -63,8 +63,8 @@ def _load():
                           ctypes.c_double, tp, tp, tp, i32p, ctypes.c_int]
             f = getattr(lib, "oracle_getrf_" + sfx)
             f.restype = ctypes.c_int
-            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, tp, tp, i32p, i32p,
-                          ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+            f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, tp, tp, i32p,
+                          i32p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         _libs[path] = lib
     return lib
@@ -139,14 +139,17 @@ def rhs_from_storage(B_store: np.ndarray, layout: str, n: int, nrhs: int) -> np.
 
 
 def gesv(A_store: np.ndarray, B_store: np.ndarray, n: int, nrhs: int, layout: str = "row",
-         nthreads: int = 0):
+         nthreads: int = 0, scale: bool = False):
     """Solve every system of a batch.
 
     ``A_store`` / ``B_store`` are the raw contiguous storage of the batch (any
     shape with batch*n*n / batch*n*nrhs elements, float32 or float64, same
     dtype).  Returns ``(X_store, piv, info)``: X in B's storage, piv int32
     [batch, n] (0-based swap sequence, all -1 for a failed system), info int32
-    [batch] (0, or the 1-based step of the first exactly zero pivot).
+    [batch]: 0; -1 for a non-finite entry of A or B; k >= 1, the 1-based step
+    of the first exactly zero pivot; -3 for a non-finite computed value.
+    ``scale`` divides each system by the largest magnitude of its matrix
+    first (the whole-matrix max-abs scaling).
     """
     sfx, ct = _sfx(A_store.dtype)
     if np.dtype(B_store.dtype) != np.dtype(A_store.dtype):
@@ -162,21 +165,24 @@ def gesv(A_store: np.ndarray, B_store: np.ndarray, n: int, nrhs: int, layout: st
     piv = np.empty((batch, n), dtype=np.int32)
     info = np.empty((batch,), dtype=np.int32)
     rc = getattr(_load(), "oracle_gesv_" + sfx)(
-        _LAYOUTS[layout], n, nrhs, batch, _ptr(A, ct), _ptr(B, ct), _ptr(X, ct),
-        _ptr(piv, ctypes.c_int32), _ptr(info, ctypes.c_int32), int(nthreads))
+        _LAYOUTS[layout], n, nrhs, batch, int(bool(scale)), _ptr(A, ct), _ptr(B, ct),
+        _ptr(X, ct), _ptr(piv, ctypes.c_int32), _ptr(info, ctypes.c_int32), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_gesv_{sfx} returned {rc}")
     return X.reshape(np.shape(B_store)), piv, info
 
 
-def getrf(A_store: np.ndarray, n: int, layout: str = "row", nthreads: int = 0):
+def getrf(A_store: np.ndarray, n: int, layout: str = "row", nthreads: int = 0,
+          scale: bool = False):
     """Factor every matrix of a batch, without stopping at a zero pivot.
 
     Returns ``(LU, ipiv, info, gap)``: LU float [batch, n, n] logical row-major
     (unit-lower L below the diagonal, U on and above it, LAPACK row order),
-    ipiv int32 [batch, n] (0-based swap sequence), info int32 [batch] and gap
-    float64 [batch], the smallest relative distance between the two largest
-    candidate magnitudes over steps 0..n-2.
+    ipiv int32 [batch, n] (0-based swap sequence), info int32 [batch] (as for
+    ``gesv``) and gap float64 [batch], the smallest relative distance between
+    the two largest candidate magnitudes over steps 0..n-2.  The factors of a
+    failed system are returned as computed (all +0.0 with ipiv -1 for status
+    -1).  ``scale``: max-abs scaling, U multiplied back at the end.
     """
     sfx, ct = _sfx(A_store.dtype)
     A = np.ascontiguousarray(A_store).reshape(-1)
@@ -188,8 +194,9 @@ def getrf(A_store: np.ndarray, n: int, layout: str = "row", nthreads: int = 0):
     info = np.empty((batch,), dtype=np.int32)
     gap = np.empty((batch,), dtype=np.float64)
     rc = getattr(_load(), "oracle_getrf_" + sfx)(
-        _LAYOUTS[layout], n, batch, _ptr(A, ct), _ptr(LU, ct), _ptr(ipiv, ctypes.c_int32),
-        _ptr(info, ctypes.c_int32), _ptr(gap, ctypes.c_double), int(nthreads))
+        _LAYOUTS[layout], n, batch, int(bool(scale)), _ptr(A, ct), _ptr(LU, ct),
+        _ptr(ipiv, ctypes.c_int32), _ptr(info, ctypes.c_int32), _ptr(gap, ctypes.c_double),
+        int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_getrf_{sfx} returned {rc}")
     return LU, ipiv, info, gap
@@ -224,8 +231,9 @@ def potrf(A_store: np.ndarray, n: int, layout: str = "row", shift: float = 0.0,
           nthreads: int = 0):
     """Cholesky factors of A + shift I.  Returns ``(L, info)``: L float
     [batch, n, n] logical row-major (lower triangular, zero above; all +0.0
-    for a failed system), info int32 [batch] (0; j+1 for the first
-    non-positive pivot; -2 for a matrix that is not exactly symmetric)."""
+    for a failed system), info int32 [batch] (0; -1 for a non-finite entry of
+    A; -2 for a matrix that is not exactly symmetric; j+1 for the first
+    non-positive pivot; -3 for a non-finite entry of L)."""
     sfx, ct = _sfx(A_store.dtype)
     A = np.ascontiguousarray(A_store).reshape(-1)
     batch = A.size // (n * n)

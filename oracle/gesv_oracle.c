@@ -34,8 +34,11 @@
  * inner products in increasing k, status j+1 for the first non-positive
  * pivot, failed systems zeroed.
  *
- * Not done here, on purpose: the whole-matrix max-abs scaling and the
- * non-finite status codes of the ruSOLVER contract (not part of this path).
+ * The non-finite statuses of the same contract hold everywhere: -1 for a
+ * non-finite input entry, -3 for a non-finite computed value (after the
+ * positive status of a failed pivot in precedence).  Its whole-matrix
+ * max-abs scaling of the LU, with the scale of U restored, is an option of
+ * gesv and getrf (`scale`).
  *
  * Built with gcc -O2 -ffp-contract=off so that no multiply-add is fused
  * except the explicit fma()/fmaf() calls, which match the GPU's fused

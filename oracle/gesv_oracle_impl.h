@@ -30,9 +30,25 @@ static size_t SFX(rhs_index)(int layout, int n, int nrhs, int r, int j)
 }
 
 /*
+ * Magnitude order of the pivot search: v ranks strictly above m.  Numbers
+ * compare as numbers; a NaN ranks above every number (IEEE 754 totalOrder
+ * places NaN beyond infinity) and equal to another NaN.  Inputs are finite
+ * (a non-finite input fails with status -1 before any step), so a NaN
+ * candidate can only be an intermediate result, and the system then fails
+ * with status -3 whatever is chosen; the order only has to be total so that
+ * the choice, and hence a zero-pivot status, is well defined.
+ */
+static int SFX(ranks_above)(REAL v, REAL m)
+{
+    if (isnan(v))
+        return !isnan(m);
+    return v > m;
+}
+
+/*
  * Partial pivoting, first maximum: scan the candidates of column k in
  * increasing current row position, replacing the running choice only when a
- * magnitude is strictly larger.  On equal magnitudes the lowest current
+ * magnitude ranks strictly above it.  On equal magnitudes the lowest current
  * position therefore wins (LAPACK's choice, the tie rule of the ruSOLVER
  * numerical contract and the first-maximum rule of the SparseDirectSolver
  * review).  Returns the position; *mag receives the winning magnitude.
@@ -43,7 +59,7 @@ static int SFX(pivot_search)(const REAL *M, int n, int k, REAL *mag)
     REAL m = FABS(M[(size_t)k * n + k]);
     for (int r = k + 1; r < n; ++r) {
         REAL v = FABS(M[(size_t)r * n + k]);
-        if (v > m) {
+        if (SFX(ranks_above)(v, m)) {
             p = r;
             m = v;
         }
@@ -61,6 +77,39 @@ static void SFX(swap_rows)(REAL *M, int width, int i, int j)
     }
 }
 
+/* 1 when every one of the count values is finite (no NaN, no infinity). */
+static int SFX(all_finite)(const REAL *v, size_t count)
+{
+    for (size_t e = 0; e < count; ++e)
+        if (!isfinite(v[e]))
+            return 0;
+    return 1;
+}
+
+/*
+ * Whole-matrix max-abs scaling (ruSOLVER page, section on the unchanged
+ * numerical and failure contract: the LU keeps its scaling by the largest
+ * absolute value of the whole matrix and restores the scale of U at the
+ * end).  Reading: the system is scaled as a whole, M / s and Y / s with
+ * s = max |M(r,c)| (each entry by IEEE division), which leaves the solution
+ * unchanged; a zero matrix (s == 0) is left as it is.  Returns s, or 1 when
+ * nothing was scaled.
+ */
+static REAL SFX(scale_system)(REAL *M, int n, REAL *Y, int nrhs)
+{
+    REAL s = 0;
+    for (size_t e = 0; e < (size_t)n * n; ++e)
+        if (FABS(M[e]) > s)
+            s = FABS(M[e]);
+    if (!(s > 0))
+        return (REAL)1;
+    for (size_t e = 0; e < (size_t)n * n; ++e)
+        M[e] = M[e] / s;
+    for (size_t e = 0; e < (size_t)n * nrhs; ++e)
+        Y[e] = Y[e] / s;
+    return s;
+}
+
 /*
  * gesv of one system.  M (n*n) and Y (n*nrhs) are scratch, logical row-major.
  *
@@ -73,11 +122,14 @@ static void SFX(swap_rows)(REAL *M, int width, int i, int j)
  * "Departures from the MAGMA kernel" (solution entry kept by its owner).
  *
  * Result contract (ruSOLVER small-matrix page, section on the unchanged
- * numerical and failure contract): status 0 on success, k >= 1 for the
- * first pivot that fails (here: an exactly zero pivot, 1-based step); a
- * failed system has every solution entry +0.0 and every pivot -1.
+ * numerical and failure contract), in this order of precedence: -1 when an
+ * entry of A or B is not finite; k >= 1 for the first pivot that fails
+ * (here: an exactly zero pivot, 1-based step); -3 when a computed value is
+ * not finite (an entry of L, U, y = L^-1 P b or x); else 0.  A failed
+ * system has every solution entry +0.0 and every pivot -1.  With `scale`
+ * the system is first scaled by its largest magnitude (scale_system).
  */
-static int SFX(gesv_one)(int layout, int n, int nrhs, const REAL *a, const REAL *b,
+static int SFX(gesv_one)(int layout, int n, int nrhs, int scale, const REAL *a, const REAL *b,
                          REAL *x, int32_t *piv, REAL *M, REAL *Y)
 {
     for (int r = 0; r < n; ++r)
@@ -88,7 +140,11 @@ static int SFX(gesv_one)(int layout, int n, int nrhs, const REAL *a, const REAL 
             Y[(size_t)r * nrhs + j] = b[SFX(rhs_index)(layout, n, nrhs, r, j)];
 
     int info = 0;
-    for (int k = 0; k < n; ++k) {
+    if (!SFX(all_finite)(M, (size_t)n * n) || !SFX(all_finite)(Y, (size_t)n * nrhs))
+        info = -1;
+    else if (scale)
+        (void)SFX(scale_system)(M, n, Y, nrhs);
+    for (int k = 0; k < n && info == 0; ++k) {
         REAL mag;
         int p = SFX(pivot_search)(M, n, k, &mag);
         piv[k] = p;
@@ -112,6 +168,25 @@ static int SFX(gesv_one)(int layout, int n, int nrhs, const REAL *a, const REAL 
         }
     }
 
+    if (info == 0 &&
+        (!SFX(all_finite)(M, (size_t)n * n) || !SFX(all_finite)(Y, (size_t)n * nrhs)))
+        info = -3; /* L, U or y */
+
+    if (info == 0) {
+        /* U x = y: x_k = y_k / u_kk, then x_k leaves the rows r < k. */
+        for (int k = n - 1; k >= 0; --k) {
+            const REAL ukk = M[(size_t)k * n + k];
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / ukk;
+            for (int r = 0; r < k; ++r)
+                for (int j = 0; j < nrhs; ++j)
+                    Y[(size_t)r * nrhs + j] =
+                        FMA(-M[(size_t)r * n + k], Y[(size_t)k * nrhs + j], Y[(size_t)r * nrhs + j]);
+        }
+        if (!SFX(all_finite)(Y, (size_t)n * nrhs))
+            info = -3; /* x */
+    }
+
     if (info != 0) {
         for (int r = 0; r < n; ++r) {
             piv[r] = -1;
@@ -119,17 +194,6 @@ static int SFX(gesv_one)(int layout, int n, int nrhs, const REAL *a, const REAL 
                 x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;
         }
         return info;
-    }
-
-    /* U x = y: x_k = y_k / u_kk, then x_k leaves the rows r < k. */
-    for (int k = n - 1; k >= 0; --k) {
-        const REAL ukk = M[(size_t)k * n + k];
-        for (int j = 0; j < nrhs; ++j)
-            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / ukk;
-        for (int r = 0; r < k; ++r)
-            for (int j = 0; j < nrhs; ++j)
-                Y[(size_t)r * nrhs + j] =
-                    FMA(-M[(size_t)r * n + k], Y[(size_t)k * nrhs + j], Y[(size_t)r * nrhs + j]);
     }
     for (int r = 0; r < n; ++r)
         for (int j = 0; j < nrhs; ++j)
@@ -149,12 +213,29 @@ static int SFX(gesv_one)(int layout, int n, int nrhs, const REAL *a, const REAL 
  * (|c1| - |c2|) / |c1| between the two largest candidate magnitudes of the
  * step (0 when the largest is 0; 1 when n == 1).  A small gap marks a pivot
  * choice that rounding could flip.
+ *
+ * Status as in gesv_one: -1 for a non-finite entry of A (lu then all +0.0,
+ * ipiv all -1, gap 0), the first zero pivot, then -3 when an entry of L or U
+ * is not finite.  With `scale`, the matrix is divided by its largest
+ * magnitude first and U is multiplied back by it at the end (the scale of U
+ * restored; L is scale-free).
  */
-static int SFX(getrf_one)(int layout, int n, const REAL *a, REAL *lu, int32_t *ipiv, double *gap)
+static int SFX(getrf_one)(int layout, int n, int scale, const REAL *a, REAL *lu, int32_t *ipiv,
+                          double *gap)
 {
     for (int r = 0; r < n; ++r)
         for (int c = 0; c < n; ++c)
             lu[(size_t)r * n + c] = SFX(load_a)(a, layout, n, r, c);
+    if (!SFX(all_finite)(lu, (size_t)n * n)) {
+        for (int r = 0; r < n; ++r) {
+            ipiv[r] = -1;
+            for (int c = 0; c < n; ++c)
+                lu[(size_t)r * n + c] = 0;
+        }
+        *gap = 0.0;
+        return -1;
+    }
+    const REAL sc = scale ? SFX(scale_system)(lu, n, NULL, 0) : (REAL)1;
 
     int info = 0;
     double g = 1.0;
@@ -193,6 +274,12 @@ static int SFX(getrf_one)(int layout, int n, const REAL *a, REAL *lu, int32_t *i
                 lu[(size_t)r * n + c] = FMA(-l, lu[(size_t)k * n + c], lu[(size_t)r * n + c]);
         }
     }
+    if (scale)
+        for (int r = 0; r < n; ++r)
+            for (int c = r; c < n; ++c)
+                lu[(size_t)r * n + c] = lu[(size_t)r * n + c] * sc;
+    if (info == 0 && !SFX(all_finite)(lu, (size_t)n * n))
+        info = -3;
     *gap = g;
     return info;
 }
@@ -297,7 +384,10 @@ int SFX(oracle_getrs)(int layout, int n, int nrhs, int64_t batch, const REAL *LU
  *  - status j+1 (1-based) for the first step whose s is not > 0 (the
  *    smallest leading minor that is not positive definite, as cuSolverDx
  *    reports it); a failed system (any nonzero status) gets L = +0.0 and
- *    x = +0.0 everywhere.
+ *    x = +0.0 everywhere;
+ *  - precedence of the statuses: -1 for a non-finite input entry (A, and B
+ *    for posv), then -2, then j+1, then -3 when a computed value (an entry
+ *    of L, y or x) is not finite.
  * The lower triangle is read; the symmetry check makes the choice moot.
  *
  * The solves: y_i = b_i - sum_{k<i} L(i,k) y_k in increasing k, then
@@ -307,6 +397,8 @@ int SFX(oracle_getrs)(int layout, int n, int nrhs, int64_t batch, const REAL *LU
  */
 static int SFX(potrf_one)(int layout, int n, REAL shift, const REAL *a, REAL *L)
 {
+    if (!SFX(all_finite)(a, (size_t)n * n))
+        return -1;
     for (int i = 0; i < n; ++i)
         for (int j = 0; j < i; ++j)
             if (!(SFX(load_a)(a, layout, n, i, j) == SFX(load_a)(a, layout, n, j, i)))
@@ -328,17 +420,22 @@ static int SFX(potrf_one)(int layout, int n, REAL shift, const REAL *a, REAL *L)
             L[(size_t)i * n + j] = t / d;
         }
     }
-    return 0;
+    return SFX(all_finite)(L, (size_t)n * n) ? 0 : -3;
+}
+
+static void SFX(zero_rhs)(int layout, int n, int nrhs, REAL *x)
+{
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;
 }
 
 static int SFX(posv_one)(int layout, int n, int nrhs, REAL shift, const REAL *a, const REAL *b,
                          REAL *x, REAL *L, REAL *Y)
 {
-    int info = SFX(potrf_one)(layout, n, shift, a, L);
+    int info = SFX(all_finite)(b, (size_t)n * nrhs) ? SFX(potrf_one)(layout, n, shift, a, L) : -1;
     if (info != 0) {
-        for (int r = 0; r < n; ++r)
-            for (int j = 0; j < nrhs; ++j)
-                x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;
+        SFX(zero_rhs)(layout, n, nrhs, x);
         return info;
     }
     for (int r = 0; r < n; ++r)
@@ -354,6 +451,10 @@ static int SFX(posv_one)(int layout, int n, int nrhs, REAL shift, const REAL *a,
                 Y[(size_t)i * nrhs + j] =
                     FMA(-L[(size_t)i * n + k], Y[(size_t)k * nrhs + j], Y[(size_t)i * nrhs + j]);
     }
+    if (!SFX(all_finite)(Y, (size_t)n * nrhs)) {
+        SFX(zero_rhs)(layout, n, nrhs, x); /* y */
+        return -3;
+    }
     /* L^T x = y */
     for (int k = n - 1; k >= 0; --k) {
         const REAL d = L[(size_t)k * n + k];
@@ -363,6 +464,10 @@ static int SFX(posv_one)(int layout, int n, int nrhs, REAL shift, const REAL *a,
             for (int j = 0; j < nrhs; ++j)
                 Y[(size_t)i * nrhs + j] =
                     FMA(-L[(size_t)k * n + i], Y[(size_t)k * nrhs + j], Y[(size_t)i * nrhs + j]);
+    }
+    if (!SFX(all_finite)(Y, (size_t)n * nrhs)) {
+        SFX(zero_rhs)(layout, n, nrhs, x); /* x */
+        return -3;
     }
     for (int r = 0; r < n; ++r)
         for (int j = 0; j < nrhs; ++j)
@@ -422,8 +527,8 @@ int SFX(oracle_posv)(int layout, int n, int nrhs, int64_t batch, double shift, c
     return failed ? ORACLE_ENOMEM : 0;
 }
 
-int SFX(oracle_gesv)(int layout, int n, int nrhs, int64_t batch, const REAL *A, const REAL *B,
-                     REAL *X, int32_t *piv, int32_t *info, int nthreads)
+int SFX(oracle_gesv)(int layout, int n, int nrhs, int64_t batch, int scale, const REAL *A,
+                     const REAL *B, REAL *X, int32_t *piv, int32_t *info, int nthreads)
 {
     int rc = oracle_check_args(layout, n, nrhs, batch);
     if (rc != 0)
@@ -443,7 +548,7 @@ int SFX(oracle_gesv)(int layout, int n, int nrhs, int64_t batch, const REAL *A, 
         } else {
 #pragma omp for schedule(static)
             for (int64_t s = 0; s < batch; ++s) {
-                info[s] = SFX(gesv_one)(layout, n, nrhs, A + s * (int64_t)n * n,
+                info[s] = SFX(gesv_one)(layout, n, nrhs, scale, A + s * (int64_t)n * n,
                                         B + s * (int64_t)n * nrhs, X + s * (int64_t)n * nrhs,
                                         piv + s * (int64_t)n, M, Y);
             }
@@ -454,8 +559,8 @@ int SFX(oracle_gesv)(int layout, int n, int nrhs, int64_t batch, const REAL *A, 
     return failed ? ORACLE_ENOMEM : 0;
 }
 
-int SFX(oracle_getrf)(int layout, int n, int64_t batch, const REAL *A, REAL *LU, int32_t *ipiv,
-                      int32_t *info, double *gap, int nthreads)
+int SFX(oracle_getrf)(int layout, int n, int64_t batch, int scale, const REAL *A, REAL *LU,
+                      int32_t *ipiv, int32_t *info, double *gap, int nthreads)
 {
     int rc = oracle_check_args(layout, n, 1, batch);
     if (rc != 0)
@@ -466,8 +571,8 @@ int SFX(oracle_getrf)(int layout, int n, int64_t batch, const REAL *A, REAL *LU,
         nthreads = omp_get_max_threads();
 #pragma omp parallel for num_threads(nthreads) schedule(static)
     for (int64_t s = 0; s < batch; ++s) {
-        info[s] = SFX(getrf_one)(layout, n, A + s * (int64_t)n * n, LU + s * (int64_t)n * n,
-                                 ipiv + s * (int64_t)n, gap + s);
+        info[s] = SFX(getrf_one)(layout, n, scale, A + s * (int64_t)n * n,
+                                 LU + s * (int64_t)n * n, ipiv + s * (int64_t)n, gap + s);
     }
     return 0;
 }

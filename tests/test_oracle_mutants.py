@@ -29,7 +29,7 @@ MUTANTS = {
                            "Y[(size_t)r * nrhs + j]);",
                            "(void)0;"),
     "rhs_swap_dropped": ("SFX(swap_rows)(Y, nrhs, k, p);", "(void)0;"),
-    "tie_to_last": ("if (v > m) {", "if (v >= m) {"),
+    "tie_to_last": ("if (SFX(ranks_above)(v, m)) {", "if (SFX(ranks_above)(v, m) || v == m) {"),
     "candidate_skipped": ("for (int r = k + 1; r < n; ++r) {\n        REAL v = FABS",
                           "for (int r = k + 2; r < n; ++r) {\n        REAL v = FABS"),
     "reciprocal_multiplier": ("const REAL l = M[(size_t)r * n + k] / d;",
@@ -66,9 +66,25 @@ MUTANTS = {
     "chol_shift_ignored": ("REAL s = SFX(load_a)(a, layout, n, j, j) + shift;",
                            "REAL s = SFX(load_a)(a, layout, n, j, j);"),
     "chol_back_transposed": ("FMA(-L[(size_t)k * n + i], Y[(size_t)k * nrhs + j], "
-                             "Y[(size_t)i * nrhs + j]);\n    }\n    for (int r = 0;",
+                             "Y[(size_t)i * nrhs + j]);\n    }\n    if (!SFX(all_finite)",
                              "FMA(-L[(size_t)i * n + k], Y[(size_t)k * nrhs + j], "
-                             "Y[(size_t)i * nrhs + j]);\n    }\n    for (int r = 0;"),
+                             "Y[(size_t)i * nrhs + j]);\n    }\n    if (!SFX(all_finite)"),
+    "nan_never_wins": ("    if (isnan(v))\n        return !isnan(m);\n", ""),
+    "input_check_dropped": ("        info = -1;\n    else if (scale)", "        info = 0;\n    else if (scale)"),
+    "factor_check_dropped": ("        info = -3; /* L, U or y */", "        info = 0;"),
+    "solution_check_dropped": ("            info = -3; /* x */", "            info = 0;"),
+    "getrf_check_dropped": ("    if (info == 0 && !SFX(all_finite)(lu, (size_t)n * n))\n        info = -3;",
+                            "    (void)0;"),
+    "scale_rhs_not_scaled": ("        Y[e] = Y[e] / s;", "        Y[e] = Y[e];"),
+    "scale_u_not_restored": ("lu[(size_t)r * n + c] = lu[(size_t)r * n + c] * sc;",
+                             "lu[(size_t)r * n + c] = lu[(size_t)r * n + c];"),
+    "scale_signed_max": ("        if (FABS(M[e]) > s)\n            s = FABS(M[e]);",
+                         "        if (M[e] > s)\n            s = M[e];"),
+    "chol_input_check_dropped": ("    if (!SFX(all_finite)(a, (size_t)n * n))\n        return -1;", ""),
+    "chol_factor_check_dropped": ("    return SFX(all_finite)(L, (size_t)n * n) ? 0 : -3;",
+                                  "    return 0;"),
+    "posv_solution_check_dropped": ("        SFX(zero_rhs)(layout, n, nrhs, x); /* x */\n        return -3;",
+                                    "        (void)0;"),
     "getrs_failed_negative_zero": (
         "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;\n        return;",
         "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = -(REAL)0;\n        return;"),
@@ -92,6 +108,12 @@ def _selection():
     yield lambda: pins.test_cholesky_exact_integer_factors(np.float32, "col")
     yield lambda: pins.test_cholesky_symmetry_and_shift(np.float64)
     yield lambda: pins.test_cholesky_first_failing_minor()
+    yield lambda: pins.test_nonfinite_input_status(np.float64, "row")
+    yield lambda: pins.test_overflow_gives_minus3(np.float32, "col")
+    yield lambda: pins.test_nan_candidate_ranks_above_zero(np.float64)
+    yield lambda: pins.test_scaling_by_power_of_two_is_exact(np.float64, "row")
+    yield lambda: pins.test_scaling_general(np.float64)
+    yield lambda: pins.test_cholesky_nonfinite_statuses(np.float32)
 
 
 def _build_variant(tmp_path, name, mutation):

@@ -616,3 +616,187 @@ def test_cholesky_symmetry_and_shift(dtype):
     # a shift that makes the first pivot non-positive fails at step 1
     _, info = oracle.potrf(A[None], n, "row", shift=-float(A[0, 0]))
     assert info[0] == 1
+
+
+# ------------------------------------------------- non-finite statuses, scaling
+#
+# ruSOLVER's status codes: -1 for a non-finite input, -3 for a non-finite
+# intermediate result, after the positive status of a failed pivot; a failed
+# system is zeroed.  The cases below are built by hand so that the status is
+# fixed by the arithmetic itself (an exact value beyond the largest finite
+# number must round to infinity).
+
+def _fmax(dtype):
+    return float(np.finfo(dtype).max)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_nonfinite_input_status(dtype, layout):
+    rng = np.random.default_rng(41)
+    n, nrhs, batch = 6, 2, 12
+    A = rng.uniform(-1, 1, (batch, n, n)).astype(dtype)
+    B = rng.uniform(-1, 1, (batch, n, nrhs)).astype(dtype)
+    X0, piv0, info0 = _solve_logical(A, B, dtype, layout)
+    assert (info0 == 0).all()
+    bad = {1: ("A", np.nan), 4: ("A", np.inf), 5: ("B", -np.inf), 9: ("B", np.nan),
+           10: ("A", -np.inf)}
+    A1, B1 = A.copy(), B.copy()
+    for s, (which, v) in bad.items():
+        if which == "A":
+            A1[s, rng.integers(n), rng.integers(n)] = v
+        else:
+            B1[s, rng.integers(n), rng.integers(nrhs)] = v
+    expect = np.where(~np.isfinite(A1).all(axis=(1, 2)) | ~np.isfinite(B1).all(axis=(1, 2)),
+                      -1, 0)
+    X, piv, info = _solve_logical(A1, B1, dtype, layout)
+    np.testing.assert_array_equal(info, expect)
+    for s in range(batch):
+        if s in bad:
+            assert (X[s] == 0).all() and not np.signbit(X[s]).any() and (piv[s] == -1).all()
+        else:   # the other systems are untouched
+            np.testing.assert_array_equal(X[s], X0[s])
+            np.testing.assert_array_equal(piv[s], piv0[s])
+    LU, ipiv, finfo, _ = _factor_logical(A1, dtype, layout)
+    np.testing.assert_array_equal(finfo, np.where(~np.isfinite(A1).all(axis=(1, 2)), -1, 0))
+    # -1 comes before a zero pivot: a singular matrix with a NaN right-hand side
+    Z = np.zeros((1, n, n), dtype)
+    Bn = np.full((1, n, 1), np.nan, dtype)
+    assert _solve_logical(Z, Bn, dtype, layout)[2][0] == -1
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_overflow_gives_minus3(dtype, layout):
+    M = 0.75 * _fmax(dtype)
+    # the update -M - 1*M = -1.5 max overflows to -inf in U(1,1)
+    A = np.array([[[1, M], [1, -M]]], dtype)
+    b = np.array([[[1], [1]]], dtype)
+    X, piv, info = _solve_logical(A, b, dtype, layout)
+    assert info[0] == -3 and (X == 0).all() and (piv == -1).all()
+    assert _factor_logical(A, dtype, layout)[2][0] == -3
+    # finite factors, but the solution 2^100 / 2^-1000 (f32: 2^20 / 2^-120)
+    # is beyond the range
+    e_small, e_big = (-1000, 100) if dtype == np.float64 else (-120, 20)
+    A = np.array([[[2.0 ** e_small]]], dtype)
+    b = np.array([[[2.0 ** e_big]]], dtype)
+    X, piv, info = _solve_logical(A, b, dtype, layout)
+    assert info[0] == -3 and X[0, 0, 0] == 0
+    assert _factor_logical(A, dtype, layout)[2][0] == 0
+    # a zero pivot comes before -3: same overflow, then a zero column
+    A = np.array([[[1, M, 0], [1, -M, 0], [0, 0, 0]]], dtype)
+    X, piv, info = _solve_logical(A, np.ones((1, 3, 1), dtype), dtype, layout)
+    assert info[0] == 3
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_nan_candidate_ranks_above_zero(dtype):
+    # Step 0 (ties to position 0) sends -inf to positions 1 and 3 of column
+    # 1; step 1 takes the first (-inf), so position 2 gets the multiplier
+    # 1/-inf = -0 and keeps an exact 0 in column 2, while position 3 gets
+    # -inf/-inf = NaN.  At step 2 the candidates are 0 (position 2) and NaN
+    # (position 3): NaN ranks above, so there is no zero pivot and the
+    # non-finite factors give -3.  A search in which NaN never wins would stop
+    # at a zero pivot (status 3).
+    M = 0.75 * _fmax(dtype)
+    A = np.array([[[1, M, 0, 0],
+                   [1, -M, 1, 0],
+                   [0, 1, 0, 1],
+                   [1, -M, 0, 0]]], dtype)
+    X, piv, info = _solve_logical(A, np.ones((1, 4, 1), dtype), dtype, "row")
+    assert info[0] == -3
+    assert _factor_logical(A, dtype, "col")[2][0] == -3
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_scaling_by_power_of_two_is_exact(dtype, layout):
+    # When the largest magnitude is a power of two, dividing by it and
+    # multiplying U back are exact, so the scaled solve and factorization
+    # are bitwise the unscaled ones.
+    rng = np.random.default_rng(43)
+    n, nrhs, batch = 9, 3, 40
+    A = rng.uniform(-1, 1, (batch, n, n))
+    e = rng.integers(-6, 7, batch)
+    for s in range(batch):
+        A[s, rng.integers(n), rng.integers(n)] = rng.choice([-1.0, 1.0])
+        A[s] *= 2.0 ** e[s]
+    A = A.astype(dtype)
+    B = rng.uniform(-1, 1, (batch, n, nrhs)).astype(dtype)
+    A_st, B_st = oracle.to_storage(A, layout), oracle.rhs_to_storage(B, layout)
+    X0, p0, i0 = oracle.gesv(A_st, B_st, n, nrhs, layout)
+    X1, p1, i1 = oracle.gesv(A_st, B_st, n, nrhs, layout, scale=True)
+    np.testing.assert_array_equal(X1, X0)
+    np.testing.assert_array_equal(p1, p0)
+    np.testing.assert_array_equal(i1, i0)
+    LU0, q0, f0, _ = oracle.getrf(A_st, n, layout)
+    LU1, q1, f1, _ = oracle.getrf(A_st, n, layout, scale=True)
+    np.testing.assert_array_equal(LU1, LU0)
+    np.testing.assert_array_equal(q1, q0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_scaling_general(dtype):
+    # Any scale: the solution is LAPACK's within the working-precision
+    # error bound, and the restored factors rebuild P A within the textbook
+    # bound.  A large common factor shows that U is restored (its scale is
+    # that of A) and that B is scaled with A (else x would be off by it).
+    rng = np.random.default_rng(44)
+    n, batch = 8, 30
+    A = (rng.normal(size=(batch, n, n)) * 37.0).astype(dtype)
+    B = rng.normal(size=(batch, n, 1)).astype(dtype)
+    X, piv, info = oracle.gesv(A, B, n, 1, "row", scale=True)
+    assert (info == 0).all()
+    u = float(np.finfo(dtype).eps)
+    for s in range(batch):
+        A64 = A[s].astype(np.float64)
+        x_ref = scipy.linalg.solve(A64, B[s].astype(np.float64))
+        kappa = np.linalg.cond(A64, np.inf)
+        err = np.abs(X[s] - x_ref).max() / np.abs(x_ref).max()
+        assert err <= 50 * n * kappa * u, (s, err)
+    LU, ipiv, finfo, _ = oracle.getrf(A, n, "row", scale=True)
+    gamma = n * u / (1 - n * u)
+    for s in range(batch):
+        L = np.tril(LU[s].astype(np.float64), -1) + np.eye(n)
+        U = np.triu(LU[s].astype(np.float64))
+        PA = A[s].astype(np.float64).copy()
+        for k in range(n):
+            PA[[k, ipiv[s, k]]] = PA[[ipiv[s, k], k]]
+        bound = 2 * gamma * np.abs(np.abs(L) @ np.abs(U)).max() + 4 * u * np.abs(U).max()
+        assert np.abs(PA - L @ U).max() <= bound, s
+    # the zero matrix is left unscaled: a zero pivot at step 1, not 0/0
+    Xz, _, iz = oracle.gesv(np.zeros((1, n, n), dtype), np.ones((1, n, 1), dtype), n, 1, "row",
+                            scale=True)
+    assert iz[0] == 1
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_cholesky_nonfinite_statuses(dtype):
+    rng = np.random.default_rng(45)
+    n = 5
+    L0, A, x, b = _exact_spd(rng, n, 1)
+    A = A.astype(dtype)
+    b = b.astype(dtype)
+    An = A.copy()
+    An[2, 3] = np.nan          # non-finite and not symmetric: -1 comes first
+    Ai = A.copy()
+    Ai[1, 1] = np.inf
+    _, info = oracle.potrf(np.stack([A, An, Ai]), n, "row")
+    assert list(info) == [0, -1, -1]
+    bn = b.copy()
+    bn[4, 0] = np.nan
+    X, info = oracle.posv(np.stack([A, A]), np.stack([b, bn]), n, 1, "row")
+    assert list(info) == [0, -1] and (X[1] == 0).all()
+    # the shift overflows the first diagonal entry: s = inf > 0, L(0,0) = inf
+    M = _fmax(dtype)
+    Ah = np.array([[[M, 1], [1, 1]]], dtype)
+    L, info = oracle.potrf(Ah, 2, "row", shift=M)
+    assert info[0] == -3 and (L == 0).all()
+    # finite factor, solution out of range: x = b / (L L^T) = 2^100 / 2^-1000
+    e_small, e_big = (-1000, 100) if dtype == np.float64 else (-120, 20)
+    X, info = oracle.posv(np.array([[[2.0 ** e_small]]], dtype),
+                          np.array([[[2.0 ** e_big]]], dtype), 1, 1, "row")
+    assert info[0] == -3 and X[0, 0, 0] == 0
+    # a non-positive pivot comes before -3
+    Aneg = np.array([[[-1, 0], [0, 1]]], dtype)
+    assert oracle.potrf(Aneg, 2, "row")[1][0] == 1
