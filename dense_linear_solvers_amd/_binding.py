@@ -38,9 +38,17 @@ class Plan(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-EXPORTED = ("tdls_gesv_batched", "tdls_getrf_batched", "tdls_getrs_batched", "tdls_plan_gesv",
-            "tdls_plan_op", "tdls_posv_batched", "tdls_potrf_batched", "tdls_strerror",
-            "tdls_version")
+class Options(ctypes.Structure):
+    """tdls_options of the *_ex calls."""
+    _fields_ = [("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("interleave", ctypes.c_int64)]
+
+
+SCALE_MAXABS = 1
+
+EXPORTED = ("tdls_gesv_batched", "tdls_gesv_batched_ex", "tdls_getrf_batched",
+            "tdls_getrf_batched_ex", "tdls_getrs_batched", "tdls_plan_gesv", "tdls_plan_op",
+            "tdls_posv_batched", "tdls_potrf_batched", "tdls_strerror", "tdls_version")
 OP_GESV, OP_GETRF, OP_GETRS, OP_POTRF, OP_POSV = 0, 1, 2, 3, 4
 _OPS = {"gesv": OP_GESV, "getrf": OP_GETRF, "getrs": OP_GETRS, "potrf": OP_POTRF,
         "posv": OP_POSV}
@@ -64,6 +72,16 @@ def load_library():
                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]
+    lib.tdls_gesv_batched_ex.restype = ctypes.c_int
+    lib.tdls_gesv_batched_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.POINTER(Options),
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_getrf_batched_ex.restype = ctypes.c_int
+    lib.tdls_getrf_batched_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.POINTER(Options),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     lib.tdls_plan_gesv.restype = ctypes.c_int
     lib.tdls_plan_gesv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int64, ctypes.POINTER(Plan)]
@@ -108,6 +126,25 @@ def tdls_gesv_batched(dtype: int, layout: int, n: int, nrhs: int, batch: int, A:
     """The C call itself, raw pointers (ints) in, return code out."""
     return int(load_library().tdls_gesv_batched(int(dtype), int(layout), int(n), int(nrhs),
                                                 int(batch), A, B, X, piv, info, stream))
+
+
+def _opt(opt):
+    return ctypes.byref(opt) if opt is not None else None
+
+
+def tdls_gesv_batched_ex(dtype: int, layout: int, n: int, nrhs: int, batch: int, opt, A: int,
+                         B: int, X: int, piv: int, info: int, stream: int) -> int:
+    """The C call with options (an Options or None), raw pointers in."""
+    return int(load_library().tdls_gesv_batched_ex(int(dtype), int(layout), int(n), int(nrhs),
+                                                   int(batch), _opt(opt), A, B, X, piv, info,
+                                                   stream))
+
+
+def tdls_getrf_batched_ex(dtype: int, layout: int, n: int, batch: int, opt, A: int, LU: int,
+                          piv: int, info: int, stream: int) -> int:
+    """The C call with options (an Options or None), raw pointers in."""
+    return int(load_library().tdls_getrf_batched_ex(int(dtype), int(layout), int(n), int(batch),
+                                                    _opt(opt), A, LU, piv, info, stream))
 
 
 def tdls_plan_gesv(dtype: int, layout: int, n: int, nrhs: int, batch: int):
@@ -174,16 +211,17 @@ def _torch():
     return torch
 
 
-def gesv_batched(A, B, layout: str = "row", out=None, stream=None):
+def gesv_batched(A, B, layout: str = "row", out=None, stream=None, scale: bool = False):
     """Solve a batch of systems held in torch CUDA tensors.
 
     A: [batch, n, n] storage of the matrices in ``layout`` (for "col" each
     A[s] holds the transpose of the logical matrix).  B: [batch, n, nrhs]
     ("row") or [batch, nrhs, n] ("col").  float32 or float64, contiguous,
     same device.  Returns (X, piv, info) with X shaped like B, piv int32
-    [batch, n], info int32 [batch].  ``out`` may pass preallocated (X, piv,
-    info).  Runs on ``stream`` (default: the current stream) and does not
-    synchronize.
+    [batch, n], info int32 [batch] (0; -1 non-finite input; k first zero
+    pivot; -3 non-finite result).  ``out`` may pass preallocated (X, piv,
+    info).  ``scale`` selects the whole-matrix max-abs scaling.  Runs on
+    ``stream`` (default: the current stream) and does not synchronize.
     """
     torch = _torch()
     if layout not in _LAYOUTS:
@@ -209,10 +247,17 @@ def gesv_batched(A, B, layout: str = "row", out=None, stream=None):
     else:
         X, piv, info = out
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    dt = F64 if A.dtype == torch.float64 else F32
     with torch.cuda.device(A.device):
-        rc = tdls_gesv_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
-                               nrhs, batch, A.data_ptr(), B.data_ptr(), X.data_ptr(),
-                               piv.data_ptr(), info.data_ptr(), s.cuda_stream)
+        if scale:
+            rc = tdls_gesv_batched_ex(dt, _LAYOUTS[layout], n, nrhs, batch,
+                                      Options(SCALE_MAXABS, 0, 1), A.data_ptr(), B.data_ptr(),
+                                      X.data_ptr(), piv.data_ptr(), info.data_ptr(),
+                                      s.cuda_stream)
+        else:
+            rc = tdls_gesv_batched(dt, _LAYOUTS[layout], n, nrhs, batch, A.data_ptr(),
+                                   B.data_ptr(), X.data_ptr(), piv.data_ptr(), info.data_ptr(),
+                                   s.cuda_stream)
     if rc != 0:
         raise TdlsError(rc, "tdls_gesv_batched")
     return X, piv, info
@@ -229,13 +274,14 @@ def _check_square(torch, A, name):
         raise ValueError(f"{name} must be [batch, n, n]")
 
 
-def getrf_batched(A, layout: str = "row", out=None, stream=None):
+def getrf_batched(A, layout: str = "row", out=None, stream=None, scale: bool = False):
     """Factor a batch of matrices held in torch CUDA tensors: P A = L U.
 
     A: [batch, n, n] storage in ``layout``.  Returns (LU, piv, info): LU like
     A (LAPACK's row order, unit-lower L below the diagonal, U on and above
     it, in the same layout), piv int32 [batch, n] (0-based swap sequence, -1
-    for a failed system), info int32 [batch].  Does not synchronize.
+    for a failed system), info int32 [batch].  ``scale``: whole-matrix
+    max-abs scaling, U multiplied back at the end.  Does not synchronize.
     """
     torch = _torch()
     if layout not in _LAYOUTS:
@@ -249,10 +295,15 @@ def getrf_batched(A, layout: str = "row", out=None, stream=None):
     else:
         LU, piv, info = out
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    dt = F64 if A.dtype == torch.float64 else F32
     with torch.cuda.device(A.device):
-        rc = tdls_getrf_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
-                                batch, A.data_ptr(), LU.data_ptr(), piv.data_ptr(),
-                                info.data_ptr(), s.cuda_stream)
+        if scale:
+            rc = tdls_getrf_batched_ex(dt, _LAYOUTS[layout], n, batch,
+                                       Options(SCALE_MAXABS, 0, 1), A.data_ptr(), LU.data_ptr(),
+                                       piv.data_ptr(), info.data_ptr(), s.cuda_stream)
+        else:
+            rc = tdls_getrf_batched(dt, _LAYOUTS[layout], n, batch, A.data_ptr(), LU.data_ptr(),
+                                    piv.data_ptr(), info.data_ptr(), s.cuda_stream)
     if rc != 0:
         raise TdlsError(rc, "tdls_getrf_batched")
     return LU, piv, info

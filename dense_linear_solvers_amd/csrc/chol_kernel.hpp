@@ -195,17 +195,25 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     asm volatile("" : "+v"(asym));
     wave_sync_lds();   // the chunk is rewritten next
   });
+  // Status, in the ruSOLVER contract's order of precedence: -1 for a
+  // non-finite input entry, -2 for a matrix that is not symmetric, the
+  // first step whose pivot is not > 0 (j + 1), then -3 when a computed value
+  // is not finite: a diagonal entry of L (nf), an entry of x, or an entry of
+  // L.  A non-finite value never turns finite again in the updates that
+  // follow, so a non-finite entry of L shows in x.
   int status;
   {
-    // one status per group: any lane of the group that saw a mismatch
-    const uint64_t m = __builtin_amdgcn_ballot_w64(asym != 0);
-    uint64_t gm;
-    if constexpr (T == 64)
-      gm = m;
-    else
-      gm = (m >> (g * T)) & ((1ull << T) - 1ull);
-    status = gm != 0 ? -2 : 0;
+    bool inbad = false;
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      sfor<0, N>([&](auto cc) { inbad |= not_finite(a[K][decltype(cc)::value]); });
+      sfor<0, NRHS>([&](auto jc) { inbad |= not_finite(y[K][decltype(jc)::value]); });
+    });
+    // one status per group: any lane of the group that saw a non-finite
+    // entry, else a mismatch
+    status = group_any<T>(inbad, g * T) ? -1 : (group_any<T>(asym != 0, g * T) ? -2 : 0);
   }
+  int nf = 0;   // a lane flag, settled at each step (asm barrier below)
 
   // ---- the explicit diagonal shift, added once to A(q,q)
   if (shift != Real(0)) {
@@ -231,6 +239,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     if (bad && status == 0) status = j + 1;
     asm volatile("" : "+v"(status));   // settled now, not at the store
     const Real d = bad ? Real(1) : sqrt_ieee(s);
+    nf |= not_finite(d);
+    asm volatile("" : "+v"(nf));
     // multipliers of the rows below j; row j itself takes d
     Real lm[R];
     sfor<0, R>([&](auto Kc) {
@@ -291,9 +301,21 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     });
   });
 
-  const bool failed = status != 0;
   if constexpr (FACT) {
     // ---- L in the layout of A, zero above the diagonal; zero when failed
+    {
+      bool bad = nf != 0;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          bad |= (q < n) & (c <= q) & not_finite(a[K][c]);
+        });
+      });
+      if (group_any<T>(bad, g * T) && status == 0) status = -3;
+    }
+    const bool failed = status != 0;
     if (live) {
       Real* Ls = X + sys * ((int64_t)n * n);
       sfor<0, R>([&](auto Kc) {
@@ -328,10 +350,12 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       if (tx == 0) info[sys] = status;
     }
   } else {
+    const bool failed = status != 0 || nf != 0;
+    bool xbad = false;
     if constexpr (NRHS == 1) {
       // ---- L^T x = y with the solver of the LU path: U = L^T, so lane c
       // writes L(c, q) into row q of the triangular store for every q <= c
-      upper_solve_store<Real, N, NRHS, T>(
+      xbad = upper_solve_store<Real, N, NRHS, T>(
           sq, tx, (int)(g * T), live, failed, live ? sys : 0, n, nrhs, col, X,
           [&](Real* yt) {
             sfor<0, R>([&](auto Kc) {
@@ -464,8 +488,18 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           });
         });
       });
+      bool bad = false;
+      sfor<0, QR>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        sfor<0, JR>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          bad |= (ph + P * m < n) & (j0 + NJ * jj < nrhs) & not_finite(xr[m][jj]);
+        });
+      });
+      xbad = group_any<T>(bad, gb);
       if (live) {
         Real* Xs = X + sys * ((int64_t)n * nrhs);
+        const bool zero = failed || xbad;
         sfor<0, QR>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
           const int q = ph + P * m;
@@ -473,7 +507,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             constexpr int jj = decltype(jc)::value;
             const int r = j0 + NJ * jj;
             if (q < n && r < nrhs) {
-              const Real v = failed ? Real(0) : xr[m][jj];
+              const Real v = zero ? Real(0) : xr[m][jj];
               if (col)
                 Xs[(int64_t)r * n + q] = v;
               else
@@ -483,6 +517,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         });
       }
     }
+    if (status == 0 && (nf != 0 || xbad)) status = -3;
     if (live) {
       if (tx == 0) info[sys] = status;
     }

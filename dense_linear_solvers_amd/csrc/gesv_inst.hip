@@ -35,7 +35,7 @@ static int launch_panel(const LaunchPlan& p, const void* A, const void* B, void*
   hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB, FACT>), dim3((unsigned)p.grid),
                      dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                      p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),
-                     static_cast<Real*>(X), piv, info);
+                     static_cast<Real*>(X), piv, info, p.flags);
   return (int)hipGetLastError();
 }
 

@@ -237,6 +237,23 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// True on every lane of the group (T lanes from gbase; the whole wave when
+// T = 64) when `v` holds on any of them.  Called by the whole wave.
+template <int T>
+__device__ __forceinline__ bool group_any(bool v, int gbase) {
+  const uint64_t b = __builtin_amdgcn_ballot_w64(v);
+  if constexpr (T == 64) {
+    return b != 0;
+  } else {
+    constexpr uint64_t GM = T == 32 ? 0xffffffffull : ((1ull << T) - 1ull);
+    return ((b >> gbase) & GM) != 0;
+  }
+}
+
+// NaN or an infinity (the status codes -1 and -3 of the ruSOLVER contract)
+__device__ __forceinline__ bool not_finite(double v) { return !__builtin_isfinite(v); }
+__device__ __forceinline__ bool not_finite(float v) { return !__builtin_isfinite(v); }
+
 __device__ __forceinline__ uint32_t hi_word(double v) {
   return (uint32_t)(__builtin_bit_cast(uint64_t, v) >> 32);
 }
@@ -253,7 +270,9 @@ __device__ __forceinline__ uint32_t lo_word(double v) {
 template <int N>
 __device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2; }
 
-// U x = y for the group's system, then X stored (all +0.0 when `failed`).
+// U x = y for the group's system, then X stored (all +0.0 when `failed` or
+// when an entry of x is not finite).  Returns true on the group's lanes
+// when an entry of x (positions below n) is not finite.
 // `ut` is the group's LDS area (at least max(N * NRHS, N (N + 1) / 2)
 // entries).  write_rhs(ut) must store the right-hand sides by position
 // (entry (q, j) at ut[q * NRHS + j]); write_u(ut) must then store row q of U
@@ -270,11 +289,12 @@ __device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2;
 // column class on the lanes of phase k % P, handed to the lanes of the same
 // class by a lane fetch; U(q, k) is read from the store.
 template <typename Real, int N, int NRHS, int T, typename WR, typename WU>
-__device__ __forceinline__ void upper_solve_store(Real* ut, int tx, int gbase, bool live,
+__device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, bool live,
                                                   bool failed, int64_t sys, int n, int nrhs,
                                                   int col, Real* X, WR&& write_rhs,
                                                   WU&& write_u) {
   constexpr int R = (N + T - 1) / T;
+  bool xbad = false;
   write_rhs(ut);
   wave_sync_lds();
   Real* Xs = X + sys * ((int64_t)n * nrhs);
@@ -346,11 +366,18 @@ __device__ __forceinline__ void upper_solve_store(Real* ut, int tx, int gbase, b
         });
       }
     });
+    bool bad = false;
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      bad |= (tx + K * T < n) & not_finite(xr[K]);
+    });
+    xbad = group_any<T>(bad, gbase);
     if (live) {
+      const bool zero = failed || xbad;
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
-        if (q < n) Xs[q] = failed ? Real(0) : xr[K];   // one column: same address in both layouts
+        if (q < n) Xs[q] = zero ? Real(0) : xr[K];   // one column: same address in both layouts
       });
     }
   } else {
@@ -391,7 +418,17 @@ __device__ __forceinline__ void upper_solve_store(Real* ut, int tx, int gbase, b
         });
       });
     });
+    bool bad = false;
+    sfor<0, QR>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      sfor<0, JR>([&](auto jc) {
+        constexpr int jj = decltype(jc)::value;
+        bad |= (ph + P * m < n) & (j0 + NJ * jj < nrhs) & not_finite(xr[m][jj]);
+      });
+    });
+    xbad = group_any<T>(bad, gbase);
     if (live) {
+      const bool zero = failed || xbad;
       sfor<0, QR>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         const int q = ph + P * m;
@@ -399,7 +436,7 @@ __device__ __forceinline__ void upper_solve_store(Real* ut, int tx, int gbase, b
           constexpr int jj = decltype(jc)::value;
           const int j = j0 + NJ * jj;
           if (q < n && j < nrhs) {
-            const Real v = failed ? Real(0) : xr[m][jj];
+            const Real v = zero ? Real(0) : xr[m][jj];
             if (col)
               Xs[(int64_t)j * n + q] = v;
             else
@@ -409,7 +446,7 @@ __device__ __forceinline__ void upper_solve_store(Real* ut, int tx, int gbase, b
       });
     }
   }
-
+  return xbad;
 }
 
 // FACT = false: gesv, X receives the solutions.  FACT = true: getrf (NRHS
@@ -419,8 +456,9 @@ template <typename Real, int N, int NRHS, int T, int B, bool FACT = false>
 __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     gesv_panel_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ A,
                       const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ piv,
-                      int32_t* __restrict__ info) {
+                      int32_t* __restrict__ info, uint32_t flags) {
   static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
+  static_assert(N > B, "the first panel has trailing columns (input check)");
   using S = PanelShape<Real, N, NRHS, T, B>;
   constexpr int R = S::R;
   constexpr int G = S::G;
@@ -532,7 +570,63 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     });
   }
 
+  // ---- whole-matrix max-abs scaling (an option; ruSOLVER page, section on
+  // the unchanged numerical and failure contract): the system is divided by
+  // the largest magnitude sc of its matrix, entry by entry (IEEE division),
+  // which leaves the solution unchanged; the factorization multiplies U back
+  // by sc at the end.  A zero (or non-finite) maximum leaves it as it is.
+  Real sc = Real(1);
+  if (flags & kFlagScaleMaxAbs) {
+    uint32_t mh = 0, ml = 0;   // lane maximum of |a|, as the bits of a non-negative value
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      sfor<0, N>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const Real v = (q < n && c < n) ? __builtin_fabs(a[K][c]) : Real(0);
+        if constexpr (is64) {
+          const uint32_t h = hi_word(v), l = lo_word(v);
+          const bool gt = h > mh || (h == mh && l > ml);
+          mh = gt ? h : mh;
+          ml = gt ? l : ml;
+        } else {
+          const uint32_t h = __builtin_bit_cast(uint32_t, v);
+          mh = h > mh ? h : mh;
+        }
+      });
+    });
+    const uint32_t gh = group_reduce<T, true>(mh);
+    Real s;
+    if constexpr (is64) {
+      const uint32_t gl = group_reduce<T, true>(mh == gh ? ml : 0u);
+      s = __builtin_bit_cast(double, ((uint64_t)gh << 32) | gl);
+    } else {
+      s = __builtin_bit_cast(float, gh);
+    }
+    sc = (s > Real(0) && !not_finite(s)) ? s : Real(1);
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      sfor<0, N>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        a[K][c] = (q < n && c < n) ? a[K][c] / sc : a[K][c];
+      });
+      sfor<0, NRHS>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        y[K][j] = (q < n && j < nrhs) ? y[K][j] / sc : y[K][j];
+      });
+    });
+  }
+
+  // Status, in the ruSOLVER contract's order of precedence: -1 for a
+  // non-finite input entry (checked column by column as the first panel
+  // reaches them), the first exactly zero pivot (k + 1), then -3 when a
+  // computed value is not finite: a pivot (nf), an entry of x, or an entry
+  // of the factors.  A non-finite value never turns finite again in the
+  // updates that follow, so a non-finite multiplier or U entry shows in x.
   int status = 0;
+  int inbad = 0;   // lane flags, settled where they are formed (asm barriers
+  int nf = 0;      // below): left to their use they keep values alive
   // Per-slot key bits for the pivot search: position << 13 | lane << 5 |
   // slot << 1 (the sign of the candidate goes in bit 0).  Positions are
   // unique, so comparing keys compares positions.
@@ -550,6 +644,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     constexpr int NT = N - k0 - bw;                    // trailing matrix columns
     constexpr int W = NT + NRHS;                       // trailing entries per row
     Real lm[B][R];                                     // multiplier, 0 unless below
+    if constexpr (k0 == 0) {
+      // input check of the panel's own columns (the others below)
+      sfor<0, R>([&](auto Kc) {
+        sfor<0, bw>([&](auto cc) { inbad |= not_finite(a[decltype(Kc)::value][decltype(cc)::value]); });
+      });
+      asm volatile("" : "+v"(inbad));
+    }
 
     sfor<0, bw>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -661,6 +762,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       else
         dpiv = __builtin_bit_cast(float, lane_fetch_u32<T>(ch, wl));
       const bool zero_pivot = dpiv == Real(0);
+      nf |= not_finite(dpiv);
+      asm volatile("" : "+v"(nf));
       if (zero_pivot && status == 0) status = k + 1;
       // settle the status here: left to the end, the per-step zero flags of
       // every step stay live in scalar registers
@@ -702,6 +805,17 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
 
     // ---- end of panel: pivot rows to LDS records, read back as DPP sources
     if constexpr (W > 0) {
+      if constexpr (k0 == 0) {
+        // input check of the trailing columns and right-hand sides, not
+        // touched before this first trailing update; -1 outranks a zero
+        // pivot of the first panel
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          sfor<bw, N>([&](auto cc) { inbad |= not_finite(a[K][decltype(cc)::value]); });
+          sfor<0, NRHS>([&](auto jc) { inbad |= not_finite(y[K][decltype(jc)::value]); });
+        });
+        status = group_any<T>(inbad != 0, gbase) ? -1 : status;
+      }
       constexpr int RECN = W + bw;                           // trailing entries + multipliers
       constexpr int NU = (W + SL - 1) / SL;                  // DPP source registers per pivot
       auto entry = [&](auto Kc, auto ec) -> Real {
@@ -772,7 +886,30 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   if constexpr (FACT) {
     // ---- factors: every row, whatever lane holds it, is row lab of L\U
     // (multipliers before its position, U from it on); a failed system gets
-    // +0.0 everywhere and pivots -1.
+    // +0.0 everywhere and pivots -1.  Under scaling, U takes its scale back.
+    if (flags & kFlagScaleMaxAbs) {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = lab[K];
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          a[K][c] = (c >= q && c < n) ? a[K][c] * sc : a[K][c];
+        });
+      });
+    }
+    {
+      bool bad = nf != 0;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = lab[K];
+        const bool real = q >= 0 && q < n;
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          bad |= real & (c < n) & not_finite(a[K][c]);
+        });
+      });
+      if (group_any<T>(bad, gbase) && status == 0) status = -3;
+    }
     const bool failed = status != 0;
     if (live) {
       Real* LUs = X + sys * ((int64_t)n * n);
@@ -818,11 +955,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   // ---- back substitution (see upper_solve_store): every row, whatever lane
   // holds it, stores its right-hand sides and then its U entries (columns
   // from its position on) by position
-  const bool failed = status != 0;
   int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
   wave_sync_lds();  // the last records have been read
-  upper_solve_store<Real, N, NRHS, T>(
-      rec, tx, gbase, live, failed, live ? sys : 0, n, nrhs, col, X,
+  const bool xbad = upper_solve_store<Real, N, NRHS, T>(
+      rec, tx, gbase, live, status != 0 || nf != 0, live ? sys : 0, n, nrhs, col, X,
       [&](Real* yt) {
         sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
@@ -848,6 +984,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           }
         });
       });
+
+  if (status == 0 && (nf != 0 || xbad)) status = -3;
+  const bool failed = status != 0;
 
   // ---- piv (all -1 for a failed system) and info
   if (live) {

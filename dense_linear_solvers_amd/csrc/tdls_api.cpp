@@ -93,6 +93,7 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   p->grid = (batch + p->systems_per_block - 1) / p->systems_per_block;
   if (p->grid > 0x7fffffffLL) return -5;
   p->shift = 0.0;
+  p->flags = 0;
   p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, T)
                  : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, NRHS, T, is64)
                                                      : gesv_lds_bytes(N, NRHS, T, is64);
@@ -124,6 +125,14 @@ int launch(const LaunchPlan& p, const void* in0, const void* in1, void* out, int
   const int err = l(p, in0, in1, out, piv, info, stream);
   if (err == (int)hipErrorInvalidConfiguration) return TDLS_ERR_NO_KERNEL;
   return err == 0 ? TDLS_SUCCESS : TDLS_ERR_LAUNCH;
+}
+
+// Options of the *_ex calls: flags allowed for the operation, reserved
+// field zero, systems one after another.
+bool bad_options(const tdls_options* opt, uint32_t allowed_flags) {
+  if (opt == nullptr) return false;
+  if ((opt->flags & ~allowed_flags) != 0 || opt->reserved != 0) return true;
+  return opt->interleave != 0 && opt->interleave != 1;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -173,57 +182,103 @@ int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nr
   return rc == -6 ? -7 : rc;
 }
 
-int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
-                      const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace tdls {
+namespace {
+
+// The pointer checks of gesv; `po` is added to the code of each pointer
+// argument (1 when an options argument comes before them).
+int gesv_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+              uint32_t flags, int po, const void* A, const void* B, void* X, int32_t* piv,
+              int32_t* info, hipStream_t stream) {
   tdls::LaunchPlan p;
   int rc = tdls::make_plan(tdls::kOpGesv, (int)dtype, (int)layout, n, nrhs, batch, &p);
   if (rc != 0) return rc;
   if (batch == 0) return TDLS_SUCCESS;  // nothing to read or write, nothing launched
+  p.flags = flags;
 
   const size_t es = dtype == TDLS_F64 ? 8 : 4;
   const size_t bytesA = (size_t)batch * n * n * es;
   const size_t bytesB = (size_t)batch * n * nrhs * es;
   const size_t bytesP = (size_t)batch * n * 4;
   const size_t bytesI = (size_t)batch * 4;
-  if (A == nullptr || tdls::misaligned(A, es)) return -6;
-  if (B == nullptr || tdls::misaligned(B, es)) return -7;
+  if (A == nullptr || tdls::misaligned(A, es)) return -6 - po;
+  if (B == nullptr || tdls::misaligned(B, es)) return -7 - po;
   if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, A, bytesA) ||
       tdls::overlaps(X, bytesB, B, bytesB))
-    return -8;
+    return -8 - po;
   if (piv == nullptr || tdls::misaligned(piv, 4) || tdls::overlaps(piv, bytesP, A, bytesA) ||
       tdls::overlaps(piv, bytesP, B, bytesB) || tdls::overlaps(piv, bytesP, X, bytesB))
-    return -9;
+    return -9 - po;
   if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
       tdls::overlaps(info, bytesI, B, bytesB) || tdls::overlaps(info, bytesI, X, bytesB) ||
       tdls::overlaps(info, bytesI, piv, bytesP))
-    return -10;
+    return -10 - po;
   return tdls::launch(p, A, B, X, piv, info, stream);
 }
 
-int tdls_getrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
-                       const void* A, void* LU, int32_t* piv, int32_t* info,
-                       hipStream_t stream) {
+int getrf_call(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, uint32_t flags,
+               int po, const void* A, void* LU, int32_t* piv, int32_t* info,
+               hipStream_t stream) {
   tdls::LaunchPlan p;
   int rc = tdls::make_plan(tdls::kOpGetrf, (int)dtype, (int)layout, n, 1, batch, &p);
   if (rc == -5) return -4;   // batch is argument 4 here
   if (rc != 0) return rc;
   if (batch == 0) return TDLS_SUCCESS;
+  p.flags = flags;
 
   const size_t es = dtype == TDLS_F64 ? 8 : 4;
   const size_t bytesA = (size_t)batch * n * n * es;
   const size_t bytesP = (size_t)batch * n * 4;
   const size_t bytesI = (size_t)batch * 4;
-  if (A == nullptr || tdls::misaligned(A, es)) return -5;
+  if (A == nullptr || tdls::misaligned(A, es)) return -5 - po;
   if (LU == nullptr || tdls::misaligned(LU, es) || tdls::overlaps(LU, bytesA, A, bytesA))
-    return -6;
+    return -6 - po;
   if (piv == nullptr || tdls::misaligned(piv, 4) || tdls::overlaps(piv, bytesP, A, bytesA) ||
       tdls::overlaps(piv, bytesP, LU, bytesA))
-    return -7;
+    return -7 - po;
   if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
       tdls::overlaps(info, bytesI, LU, bytesA) || tdls::overlaps(info, bytesI, piv, bytesP))
-    return -8;
+    return -8 - po;
   return tdls::launch(p, A, nullptr, LU, piv, info, stream);
+}
+
+}  // namespace
+}  // namespace tdls
+
+extern "C" {
+
+int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                      const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
+                      hipStream_t stream) {
+  return tdls::gesv_call(dtype, layout, n, nrhs, batch, 0u, 0, A, B, X, piv, info, stream);
+}
+
+int tdls_gesv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                         const tdls_options* opt, const void* A, const void* B, void* X,
+                         int32_t* piv, int32_t* info, hipStream_t stream) {
+  const int rc = tdls::check_scalars((int)dtype, (int)layout, n, nrhs, batch);
+  if (rc != 0) return rc;
+  if (tdls::bad_options(opt, TDLS_SCALE_MAXABS)) return -6;
+  return tdls::gesv_call(dtype, layout, n, nrhs, batch, opt ? opt->flags : 0u, 1, A, B, X, piv,
+                         info, stream);
+}
+
+int tdls_getrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                       const void* A, void* LU, int32_t* piv, int32_t* info,
+                       hipStream_t stream) {
+  return tdls::getrf_call(dtype, layout, n, batch, 0u, 0, A, LU, piv, info, stream);
+}
+
+int tdls_getrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                          const tdls_options* opt, const void* A, void* LU, int32_t* piv,
+                          int32_t* info, hipStream_t stream) {
+  const int rc = tdls::check_scalars((int)dtype, (int)layout, n, 1, batch);
+  if (rc != 0) return rc == -5 ? -4 : rc;
+  if (tdls::bad_options(opt, TDLS_SCALE_MAXABS)) return -5;
+  return tdls::getrf_call(dtype, layout, n, batch, opt ? opt->flags : 0u, 1, A, LU, piv, info,
+                          stream);
 }
 
 int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
@@ -300,12 +355,13 @@ const char* tdls_strerror(int code) {
     case -2: return "argument 2 is invalid (layout, or dtype for tdls_plan_op)";
     case -3: return "argument 3 is invalid (n outside 1..64, or layout for tdls_plan_op)";
     case -4: return "argument 4 is invalid (nrhs outside 1..8; batch for getrf; n for plan_op)";
-    case -5: return "argument 5 is invalid (batch; A for getrf; shift for potrf; nrhs for plan_op)";
-    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; shift for posv; batch for plan_op)";
+    case -5: return "argument 5 is invalid (batch; A for getrf; shift for potrf; nrhs for plan_op; options for getrf_ex)";
+    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; shift for posv; batch for plan_op; options for gesv_ex)";
     case -7: return "argument 7 is invalid (null, misaligned or overlapping buffer)";
     case -8: return "argument 8 is invalid (null, misaligned or overlapping buffer)";
     case -9: return "argument 9 is invalid (null, misaligned or overlapping buffer)";
     case -10: return "argument 10 is invalid (null, misaligned or overlapping buffer)";
+    case -11: return "argument 11 is invalid (null, misaligned or overlapping buffer)";
     case TDLS_ERR_LAUNCH: return "the kernel launch failed";
     case TDLS_ERR_DEVICE: return "the current device is not an MI355X (gfx950)";
     case TDLS_ERR_HIP: return "a HIP runtime query failed";

@@ -37,6 +37,10 @@ constexpr int kWaveSize = 64;
 // float64 systems would need 81 KiB and leave one wave per SIMD).
 constexpr int kWavesPerBlock = 1;
 
+// Options of a call (tdls_options.flags): whole-matrix max-abs scaling of
+// the LU (gesv, getrf).
+constexpr uint32_t kFlagScaleMaxAbs = 1u;
+
 // Operations the library launches.
 enum OpKind : int { kOpGesv = 0, kOpGetrf = 1, kOpGetrs = 2, kOpPotrf = 3, kOpPosv = 4 };
 
@@ -52,6 +56,7 @@ struct LaunchPlan {
   int G;              // systems per wave, 64 / T
   int64_t batch;
   double shift;       // Cholesky: explicit diagonal shift (0 otherwise)
+  uint32_t flags;     // kFlag* options of the call
   int64_t systems_per_block;
   int64_t grid;
   int threads_per_block;

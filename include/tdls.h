@@ -100,10 +100,17 @@ typedef struct tdls_plan {
  *   [9] piv     device pointer, int32 [batch][n]; written.  piv[s][k] is the
  *               0-based row exchanged with row k at step k (LAPACK's swap
  *               sequence), or -1 everywhere for a failed system.
- *  [10] info    device pointer, int32 [batch]; written.  0 on success, or
- *               k >= 1 when the pivot of step k (1-based) is exactly zero
- *               (the first such step).  A failed system gets X = +0.0 and
- *               piv = -1 in every entry.
+ *  [10] info    device pointer, int32 [batch]; written.  The status of
+ *               the ruSOLVER contract, in this order of precedence:
+ *                 -1  an entry of A or B is NaN or infinite;
+ *                 k   (k >= 1) the pivot of step k (1-based) is exactly
+ *                     zero, the first such step;
+ *                 -3  a computed value is NaN or infinite (an entry of L,
+ *                     U, L^-1 P b or x, e.g. after an overflow);
+ *                 0   success.
+ *               A failed system (info != 0) gets X = +0.0 and piv = -1 in
+ *               every entry.  A NaN arising in a pivot search ranks above
+ *               every number, so the zero-pivot status stays well defined.
  *       stream  HIP stream (0 = the null stream).
  *
  * Every output entry of every system is written, so outputs need no
@@ -117,8 +124,7 @@ typedef struct tdls_plan {
  * and the call returns at once; results are valid once the stream has
  * reached that point.  Arguments are validated before anything is
  * enqueued; on error nothing is launched.  Results do not depend on the
- * group size chosen by the planner.  Non-finite inputs are accepted but
- * their results are unspecified.
+ * group size chosen by the planner.
  *
  * Returns TDLS_SUCCESS, -i for an invalid i-th argument, or one of the
  * TDLS_ERR_* codes.
@@ -162,10 +168,11 @@ int tdls_plan_gesv(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_
  *   [7] piv     device, int32 [batch][n]; written: the 0-based swap
  *               sequence (piv[s][k] >= k), or -1 everywhere for a failed
  *               system.
- *   [8] info    device, int32 [batch]; written: 0, or the 1-based step of
- *               the first exactly zero pivot.  A failed system gets LU =
- *               +0.0 and piv = -1 in every entry (its factors are not
- *               usable, per the ruSOLVER contract).
+ *   [8] info    device, int32 [batch]; written: as for tdls_gesv_batched,
+ *               with -1 for a non-finite entry of A and -3 for a non-finite
+ *               entry of L or U.  A failed system gets LU = +0.0 and piv =
+ *               -1 in every entry (its factors are not usable, per the
+ *               ruSOLVER contract).
  *       stream  HIP stream.
  * Ownership, stream semantics and errors as for tdls_gesv_batched.
  */
@@ -213,8 +220,10 @@ int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, in
  *     and nothing else is added;
  *   - inner products accumulate in increasing k, one fused multiply-add per
  *     term; L(j,j) is the IEEE square root, L(i,j) an IEEE quotient;
- *   - info = j >= 1 for the smallest leading minor that is not positive
- *     definite (the first step whose diagonal is not > 0), else 0;
+ *   - info, in this order of precedence: -1 for a NaN or infinite entry
+ *     of A; -2 as above; j >= 1 for the smallest leading minor that is not
+ *     positive definite (the first step whose diagonal is not > 0); -3 for
+ *     a NaN or infinite entry of L (e.g. an overflowing shift); else 0;
  *   - a failed system (info != 0) gets L = +0.0 everywhere.
  *
  * Arguments (-i on rejection):
@@ -235,8 +244,9 @@ int tdls_potrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batc
  * Solve (A_s + shift I) X_s = B_s by Cholesky (LAPACK's posv): the
  * factorization of tdls_potrf_batched with L y = b folded into its steps,
  * then L^T x = y, each x_j = y_j / L(j,j) by IEEE division and removed from
- * the rows above by fused multiply-adds.  Same status; a failed system
- * gets X = +0.0.
+ * the rows above by fused multiply-adds.  Same status, with -1 also for a
+ * non-finite entry of B and -3 also for one of y or x; a failed system gets
+ * X = +0.0.
  *
  * Arguments (-i on rejection):
  *   [1] dtype, [2] layout, [3] n (1..64), [4] nrhs (1..8), [5] batch.
@@ -249,6 +259,49 @@ int tdls_potrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batc
 int tdls_posv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                       double shift, const void* A, const void* B, void* X, int32_t* info,
                       hipStream_t stream);
+
+/* Options of the *_ex calls. */
+#define TDLS_SCALE_MAXABS 1u /* flags: whole-matrix max-abs scaling of the LU */
+
+typedef struct tdls_options {
+  uint32_t flags;     /* 0, or TDLS_SCALE_MAXABS (gesv and getrf only) */
+  uint32_t reserved;  /* must be 0 */
+  int64_t interleave; /* how systems are laid out: 0 or 1, one after another
+                         (the layout of the plain calls); other values are
+                         rejected */
+} tdls_options;
+
+/*
+ * tdls_gesv_batched with options (opt may be NULL: no options).
+ *
+ * TDLS_SCALE_MAXABS ("ruSOLVER：小矩阵 kernel 优化（实验性）", section on the
+ * unchanged numerical and failure contract: the LU keeps its scaling by
+ * the largest absolute value of the whole matrix and restores the scale of
+ * U at the end): each system is divided, entry by entry (IEEE division),
+ * by s = max |A(r,c)| over its matrix, right-hand sides included, which
+ * leaves the solution unchanged; a zero matrix is not scaled.  The status
+ * is decided on the scaled system (a non-finite input still gives -1).
+ *
+ * Arguments: [1]..[5] as for tdls_gesv_batched, [6] opt (-6 for an unknown
+ * flag, a nonzero reserved field or an unsupported interleave), [7] A,
+ * [8] B, [9] X, [10] piv, [11] info, stream.
+ */
+int tdls_gesv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                         const tdls_options* opt, const void* A, const void* B, void* X,
+                         int32_t* piv, int32_t* info, hipStream_t stream);
+
+/*
+ * tdls_getrf_batched with options (opt may be NULL).  With
+ * TDLS_SCALE_MAXABS the matrix is divided by its largest magnitude s before
+ * the elimination and U is multiplied back by s at the end (its scale
+ * restored; L is scale-free); the -3 status covers the restored U.
+ *
+ * Arguments: [1]..[4] as for tdls_getrf_batched, [5] opt, [6] A, [7] LU,
+ * [8] piv, [9] info, stream.
+ */
+int tdls_getrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                          const tdls_options* opt, const void* A, void* LU, int32_t* piv,
+                          int32_t* info, hipStream_t stream);
 
 /*
  * tdls_plan_gesv for any operation: [1] op, then the scalar arguments of

@@ -52,9 +52,11 @@ class Report:
 
 
 def compare(A_st: np.ndarray, B_st: np.ndarray, X_st: np.ndarray, piv: np.ndarray,
-            info: np.ndarray, n: int, nrhs: int, layout: str, idx=None) -> Report:
+            info: np.ndarray, n: int, nrhs: int, layout: str, idx=None,
+            scale: bool = False) -> Report:
     """Compare GPU outputs with the oracle on the systems ``idx`` (all by
-    default).  Arrays are host copies in storage order."""
+    default).  Arrays are host copies in storage order.  ``scale``: the
+    outputs come from the max-abs scaled solve."""
     dt = np.dtype(A_st.dtype)
     A_st = A_st.reshape(-1, n * n)
     B_st = B_st.reshape(-1, n * nrhs)
@@ -66,8 +68,8 @@ def compare(A_st: np.ndarray, B_st: np.ndarray, X_st: np.ndarray, piv: np.ndarra
         A_st, B_st, X_st, piv, info = A_st[idx], B_st[idx], X_st[idx], piv[idx], info[idx]
     A_st = np.ascontiguousarray(A_st)
     B_st = np.ascontiguousarray(B_st)
-    Xo, pivo, infoo = oracle.gesv(A_st, B_st, n, nrhs, layout)
-    _, _, _, gap = oracle.getrf(A_st, n, layout)
+    Xo, pivo, infoo = oracle.gesv(A_st, B_st, n, nrhs, layout, scale=scale)
+    _, _, _, gap = oracle.getrf(A_st, n, layout, scale=scale)
 
     A = oracle.from_storage(A_st, layout, n)
     B = oracle.rhs_from_storage(B_st, layout, n, nrhs)

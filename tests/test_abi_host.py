@@ -227,3 +227,41 @@ def test_cholesky_validation_before_launch(lib):
     per_group = max(ch * 33, 32 * 33 // 2, 32 * 1)
     assert p["lds_bytes"] == p["systems_per_wave"] * per_group * 8
     assert tdls.plan_op("potrf", "f32", "row", 13, 5, 10)["nrhs_kernel"] == 1
+
+
+def test_options_validation_before_launch(lib):
+    n, nrhs, batch = 16, 2, 10
+    es = 8
+    a = 1 << 40                                  # never dereferenced: every call fails
+    b = a + batch * n * n * es                   # before the device is queried
+    x = b + batch * n * nrhs * es
+    pv = x + batch * n * nrhs * es
+    inf = pv + batch * n * 4
+    Opt = tdls.Options
+    g = lambda opt, *p: tdls.tdls_gesv_batched_ex(tdls.F64, tdls.ROW_MAJOR, n, nrhs, batch, opt,
+                                                  *p, 0)
+    # scalar arguments first, then the options, then the pointers (shifted by one)
+    assert tdls.tdls_gesv_batched_ex(9, 0, n, nrhs, batch, None, a, b, x, pv, inf, 0) == -1
+    assert tdls.tdls_gesv_batched_ex(1, 0, n, nrhs, -2, Opt(8, 0, 1), a, b, x, pv, inf, 0) == -5
+    assert g(Opt(2, 0, 1), a, b, x, pv, inf) == -6      # unknown flag
+    assert g(Opt(1, 7, 1), a, b, x, pv, inf) == -6      # reserved field
+    assert g(Opt(1, 0, 5), a, b, x, pv, inf) == -6      # interleave not supported here
+    assert g(Opt(1, 0, -1), a, b, x, pv, inf) == -6
+    assert g(None, 0, b, x, pv, inf) == -7
+    assert g(Opt(1, 0, 0), a, 0, x, pv, inf) == -8
+    assert g(Opt(1, 0, 1), a, b, a, pv, inf) == -9
+    assert g(Opt(1, 0, 1), a, b, x, x, inf) == -10
+    assert g(Opt(1, 0, 1), a, b, x, pv, pv) == -11
+    assert tdls.tdls_gesv_batched_ex(1, 0, n, nrhs, 0, Opt(1, 0, 1), 0, 0, 0, 0, 0, 0) == 0
+    f = lambda opt, *p: tdls.tdls_getrf_batched_ex(tdls.F64, tdls.COL_MAJOR, n, batch, opt, *p, 0)
+    lu = a + batch * n * n * es
+    pv = lu + batch * n * n * es
+    inf = pv + batch * n * 4
+    assert tdls.tdls_getrf_batched_ex(1, 0, n, -1, None, a, lu, pv, inf, 0) == -4
+    assert f(Opt(3, 0, 1), a, lu, pv, inf) == -5
+    assert f(Opt(1, 0, 1), 0, lu, pv, inf) == -6
+    assert f(Opt(1, 0, 1), a, a, pv, inf) == -7
+    assert f(None, a, lu, 0, inf) == -8
+    assert f(None, a, lu, pv, pv) == -9
+    for code in (-11,):
+        assert "unknown" not in tdls.strerror(code)
