@@ -13,13 +13,15 @@ from ._binding import (COL_MAJOR, EXPORTED, F32, F64, OP_GESV, OP_GETRF, OP_GETR
                        getrf_batched, getrs_batched, library_path, load_library, plan_gesv,
                        plan_op, posv_batched, potrf_batched, strerror, tdls_gesv_batched,
                        tdls_gesv_batched_ex, tdls_getrf_batched, tdls_getrf_batched_ex,
-                       tdls_getrs_batched, tdls_plan_gesv, tdls_plan_op, tdls_posv_batched,
-                       tdls_potrf_batched, version)
+                       tdls_getrs_batched, tdls_getrs_batched_ex, tdls_plan_gesv, tdls_plan_op,
+                       tdls_posv_batched, tdls_posv_batched_ex, tdls_potrf_batched,
+                       tdls_potrf_batched_ex, version)
 
 __all__ = ["gesv_batched", "getrf_batched", "getrs_batched", "potrf_batched", "posv_batched",
            "plan_gesv", "plan_op", "strerror", "version", "library_path", "load_library",
            "tdls_gesv_batched", "tdls_gesv_batched_ex", "tdls_getrf_batched",
-           "tdls_getrf_batched_ex", "tdls_getrs_batched", "tdls_potrf_batched",
-           "tdls_posv_batched", "tdls_plan_gesv", "tdls_plan_op", "TdlsError", "Plan", "EXPORTED",
+           "tdls_getrf_batched_ex", "tdls_getrs_batched", "tdls_getrs_batched_ex",
+           "tdls_potrf_batched", "tdls_potrf_batched_ex", "tdls_posv_batched",
+           "tdls_posv_batched_ex", "tdls_plan_gesv", "tdls_plan_op", "TdlsError", "Plan", "EXPORTED",
            "F32", "F64", "ROW_MAJOR", "COL_MAJOR", "Options", "SCALE_MAXABS", "OP_GESV", "OP_GETRF", "OP_GETRS", "OP_POTRF",
            "OP_POSV"]

@@ -47,8 +47,9 @@ class Options(ctypes.Structure):
 SCALE_MAXABS = 1
 
 EXPORTED = ("tdls_gesv_batched", "tdls_gesv_batched_ex", "tdls_getrf_batched",
-            "tdls_getrf_batched_ex", "tdls_getrs_batched", "tdls_plan_gesv", "tdls_plan_op",
-            "tdls_posv_batched", "tdls_potrf_batched", "tdls_strerror", "tdls_version")
+            "tdls_getrf_batched_ex", "tdls_getrs_batched", "tdls_getrs_batched_ex",
+            "tdls_plan_gesv", "tdls_plan_op", "tdls_posv_batched", "tdls_posv_batched_ex",
+            "tdls_potrf_batched", "tdls_potrf_batched_ex", "tdls_strerror", "tdls_version")
 OP_GESV, OP_GETRF, OP_GETRS, OP_POTRF, OP_POSV = 0, 1, 2, 3, 4
 _OPS = {"gesv": OP_GESV, "getrf": OP_GETRF, "getrs": OP_GETRS, "potrf": OP_POTRF,
         "posv": OP_POSV}
@@ -82,6 +83,22 @@ def load_library():
                                           ctypes.c_int64, ctypes.POINTER(Options),
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_getrs_batched_ex.restype = ctypes.c_int
+    lib.tdls_getrs_batched_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.POINTER(Options),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_potrf_batched_ex.restype = ctypes.c_int
+    lib.tdls_potrf_batched_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.c_double,
+                                          ctypes.POINTER(Options), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_posv_batched_ex.restype = ctypes.c_int
+    lib.tdls_posv_batched_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.c_double,
+                                         ctypes.POINTER(Options), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
     lib.tdls_plan_gesv.restype = ctypes.c_int
     lib.tdls_plan_gesv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int64, ctypes.POINTER(Plan)]
@@ -145,6 +162,29 @@ def tdls_getrf_batched_ex(dtype: int, layout: int, n: int, batch: int, opt, A: i
     """The C call with options (an Options or None), raw pointers in."""
     return int(load_library().tdls_getrf_batched_ex(int(dtype), int(layout), int(n), int(batch),
                                                     _opt(opt), A, LU, piv, info, stream))
+
+
+def tdls_getrs_batched_ex(dtype: int, layout: int, n: int, nrhs: int, batch: int, opt, LU: int,
+                          piv: int, B: int, X: int, stream: int) -> int:
+    """The C call with options (an Options or None), raw pointers in."""
+    return int(load_library().tdls_getrs_batched_ex(int(dtype), int(layout), int(n), int(nrhs),
+                                                    int(batch), _opt(opt), LU, piv, B, X,
+                                                    stream))
+
+
+def tdls_potrf_batched_ex(dtype: int, layout: int, n: int, batch: int, shift: float, opt, A: int,
+                          L: int, info: int, stream: int) -> int:
+    """The C call with options (an Options or None), raw pointers in."""
+    return int(load_library().tdls_potrf_batched_ex(int(dtype), int(layout), int(n), int(batch),
+                                                    float(shift), _opt(opt), A, L, info, stream))
+
+
+def tdls_posv_batched_ex(dtype: int, layout: int, n: int, nrhs: int, batch: int, shift: float,
+                         opt, A: int, B: int, X: int, info: int, stream: int) -> int:
+    """The C call with options (an Options or None), raw pointers in."""
+    return int(load_library().tdls_posv_batched_ex(int(dtype), int(layout), int(n), int(nrhs),
+                                                   int(batch), float(shift), _opt(opt), A, B, X,
+                                                   info, stream))
 
 
 def tdls_plan_gesv(dtype: int, layout: int, n: int, nrhs: int, batch: int):
@@ -211,56 +251,17 @@ def _torch():
     return torch
 
 
-def gesv_batched(A, B, layout: str = "row", out=None, stream=None, scale: bool = False):
-    """Solve a batch of systems held in torch CUDA tensors.
+def _dtype_code(torch, A):
+    return F64 if A.dtype == torch.float64 else F32
 
-    A: [batch, n, n] storage of the matrices in ``layout`` (for "col" each
-    A[s] holds the transpose of the logical matrix).  B: [batch, n, nrhs]
-    ("row") or [batch, nrhs, n] ("col").  float32 or float64, contiguous,
-    same device.  Returns (X, piv, info) with X shaped like B, piv int32
-    [batch, n], info int32 [batch] (0; -1 non-finite input; k first zero
-    pivot; -3 non-finite result).  ``out`` may pass preallocated (X, piv,
-    info).  ``scale`` selects the whole-matrix max-abs scaling.  Runs on
-    ``stream`` (default: the current stream) and does not synchronize.
-    """
-    torch = _torch()
-    if layout not in _LAYOUTS:
-        raise ValueError("layout must be 'row' or 'col'")
+
+def _check_pair(torch, A, B, nameA="A", nameB="B"):
     if A.dtype not in (torch.float32, torch.float64) or B.dtype != A.dtype:
-        raise TypeError("A and B must both be float32 or both float64")
+        raise TypeError(f"{nameA} and {nameB} must both be float32 or both float64")
     if not (A.is_cuda and B.is_cuda) or A.device != B.device:
-        raise ValueError("A and B must be CUDA tensors on the same device")
+        raise ValueError(f"{nameA} and {nameB} must be CUDA tensors on the same device")
     if not (A.is_contiguous() and B.is_contiguous()):
-        raise ValueError("A and B must be contiguous")
-    if A.dim() != 3 or A.shape[1] != A.shape[2]:
-        raise ValueError("A must be [batch, n, n]")
-    batch, n = A.shape[0], A.shape[1]
-    if B.dim() != 3 or B.shape[0] != batch:
-        raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
-    nrhs = B.shape[2] if layout == "row" else B.shape[1]
-    if (B.shape[1] if layout == "row" else B.shape[2]) != n:
-        raise ValueError("B does not match n")
-    if out is None:
-        X = torch.empty_like(B)
-        piv = torch.empty((batch, n), dtype=torch.int32, device=A.device)
-        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
-    else:
-        X, piv, info = out
-    s = stream if stream is not None else torch.cuda.current_stream(A.device)
-    dt = F64 if A.dtype == torch.float64 else F32
-    with torch.cuda.device(A.device):
-        if scale:
-            rc = tdls_gesv_batched_ex(dt, _LAYOUTS[layout], n, nrhs, batch,
-                                      Options(SCALE_MAXABS, 0, 1), A.data_ptr(), B.data_ptr(),
-                                      X.data_ptr(), piv.data_ptr(), info.data_ptr(),
-                                      s.cuda_stream)
-        else:
-            rc = tdls_gesv_batched(dt, _LAYOUTS[layout], n, nrhs, batch, A.data_ptr(),
-                                   B.data_ptr(), X.data_ptr(), piv.data_ptr(), info.data_ptr(),
-                                   s.cuda_stream)
-    if rc != 0:
-        raise TdlsError(rc, "tdls_gesv_batched")
-    return X, piv, info
+        raise ValueError(f"{nameA} and {nameB} must be contiguous")
 
 
 def _check_square(torch, A, name):
@@ -274,128 +275,234 @@ def _check_square(torch, A, name):
         raise ValueError(f"{name} must be [batch, n, n]")
 
 
-def getrf_batched(A, layout: str = "row", out=None, stream=None, scale: bool = False):
+def _interleaved_dims(A, B, layout: str, interleave: int, batch):
+    """Problem sizes of interleaved operands: A [blocks, n, n, W] and B
+    [blocks, n, nrhs, W] ("row") or [blocks, nrhs, n, W] ("col"), system s
+    in slice [s // W, ..., s % W]; ``batch`` defaults to blocks * W."""
+    W = int(interleave)
+    if A.dim() != 4 or A.shape[1] != A.shape[2] or A.shape[3] != W:
+        raise ValueError("interleaved A must be [blocks, n, n, W]")
+    blocks, n = A.shape[0], A.shape[1]
+    b = blocks * W if batch is None else int(batch)
+    if not ((blocks - 1) * W < b <= blocks * W or (b == 0 and blocks == 0)):
+        raise ValueError("batch does not match the interleaved blocks")
+    nrhs = None
+    if B is not None:
+        if B.dim() != 4 or B.shape[0] != blocks or B.shape[3] != W:
+            raise ValueError("interleaved B must be [blocks, n, nrhs, W] (row) or "
+                             "[blocks, nrhs, n, W] (col)")
+        nrhs = B.shape[2] if layout == "row" else B.shape[1]
+        if (B.shape[1] if layout == "row" else B.shape[2]) != n:
+            raise ValueError("B does not match n")
+    return b, n, nrhs
+
+
+def _plain_dims(A, B, layout):
+    if A.dim() != 3 or A.shape[1] != A.shape[2]:
+        raise ValueError("A must be [batch, n, n]")
+    batch, n = A.shape[0], A.shape[1]
+    nrhs = None
+    if B is not None:
+        if B.dim() != 3 or B.shape[0] != batch:
+            raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
+        nrhs = B.shape[2] if layout == "row" else B.shape[1]
+        if (B.shape[1] if layout == "row" else B.shape[2]) != n:
+            raise ValueError("B does not match n")
+    return batch, n, nrhs
+
+
+def _dims(A, B, layout, interleave, batch):
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'row' or 'col'")
+    if interleave > 1:
+        return _interleaved_dims(A, B, layout, interleave, batch)
+    if batch is not None and batch != A.shape[0]:
+        raise ValueError("batch is given by A's first dimension")
+    return _plain_dims(A, B, layout)
+
+
+def _piv_shape(A, n, interleave):
+    return (A.shape[0], n, interleave) if interleave > 1 else (A.shape[0], n)
+
+
+def _options(flags, interleave):
+    return Options(flags, 0, max(1, int(interleave)))
+
+
+# Interleaved batches (``interleave`` W > 1): the operands are 4-D, A
+# [blocks, n, n, W] (its [b, :, :, w] slice is system b*W + w in ``layout``),
+# B and X [blocks, n, nrhs, W] ("row") or [blocks, nrhs, n, W] ("col"), piv
+# [blocks, n, W]; info stays [batch].  ``batch`` may end inside the last
+# block.  W = 1 (default): the 3-D operands of the plain calls.
+
+
+def gesv_batched(A, B, layout: str = "row", out=None, stream=None, scale: bool = False,
+                 interleave: int = 1, batch=None):
+    """Solve a batch of systems held in torch CUDA tensors.
+
+    A: [batch, n, n] storage of the matrices in ``layout`` (for "col" each
+    A[s] holds the transpose of the logical matrix).  B: [batch, n, nrhs]
+    ("row") or [batch, nrhs, n] ("col").  float32 or float64, contiguous,
+    same device.  Returns (X, piv, info) with X shaped like B, piv int32
+    [batch, n], info int32 [batch] (0; -1 non-finite input; k first zero
+    pivot; -3 non-finite result).  ``out`` may pass preallocated (X, piv,
+    info).  ``scale`` selects the whole-matrix max-abs scaling;
+    ``interleave`` an interleaved batch (see above).  Runs on ``stream``
+    (default: the current stream) and does not synchronize.
+    """
+    torch = _torch()
+    _check_pair(torch, A, B)
+    nb, n, nrhs = _dims(A, B, layout, interleave, batch)
+    if out is None:
+        X = torch.empty_like(B)
+        piv = torch.empty(_piv_shape(A, n, interleave), dtype=torch.int32, device=A.device)
+        info = torch.empty((nb,), dtype=torch.int32, device=A.device)
+    else:
+        X, piv, info = out
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    dt = _dtype_code(torch, A)
+    with torch.cuda.device(A.device):
+        if scale or interleave > 1:
+            rc = tdls_gesv_batched_ex(dt, _LAYOUTS[layout], n, nrhs, nb,
+                                      _options(SCALE_MAXABS if scale else 0, interleave),
+                                      A.data_ptr(), B.data_ptr(), X.data_ptr(), piv.data_ptr(),
+                                      info.data_ptr(), s.cuda_stream)
+        else:
+            rc = tdls_gesv_batched(dt, _LAYOUTS[layout], n, nrhs, nb, A.data_ptr(),
+                                   B.data_ptr(), X.data_ptr(), piv.data_ptr(), info.data_ptr(),
+                                   s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_gesv_batched")
+    return X, piv, info
+
+
+def getrf_batched(A, layout: str = "row", out=None, stream=None, scale: bool = False,
+                  interleave: int = 1, batch=None):
     """Factor a batch of matrices held in torch CUDA tensors: P A = L U.
 
     A: [batch, n, n] storage in ``layout``.  Returns (LU, piv, info): LU like
     A (LAPACK's row order, unit-lower L below the diagonal, U on and above
     it, in the same layout), piv int32 [batch, n] (0-based swap sequence, -1
     for a failed system), info int32 [batch].  ``scale``: whole-matrix
-    max-abs scaling, U multiplied back at the end.  Does not synchronize.
+    max-abs scaling, U multiplied back at the end.  ``interleave``: an
+    interleaved batch.  Does not synchronize.
     """
     torch = _torch()
-    if layout not in _LAYOUTS:
-        raise ValueError("layout must be 'row' or 'col'")
-    _check_square(torch, A, "A")
-    batch, n = A.shape[0], A.shape[1]
+    if A.dtype not in (torch.float32, torch.float64) or not A.is_cuda or not A.is_contiguous():
+        raise ValueError("A must be a contiguous float32 or float64 CUDA tensor")
+    nb, n, _ = _dims(A, None, layout, interleave, batch)
     if out is None:
         LU = torch.empty_like(A)
-        piv = torch.empty((batch, n), dtype=torch.int32, device=A.device)
-        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+        piv = torch.empty(_piv_shape(A, n, interleave), dtype=torch.int32, device=A.device)
+        info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
         LU, piv, info = out
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
-    dt = F64 if A.dtype == torch.float64 else F32
+    dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):
-        if scale:
-            rc = tdls_getrf_batched_ex(dt, _LAYOUTS[layout], n, batch,
-                                       Options(SCALE_MAXABS, 0, 1), A.data_ptr(), LU.data_ptr(),
-                                       piv.data_ptr(), info.data_ptr(), s.cuda_stream)
+        if scale or interleave > 1:
+            rc = tdls_getrf_batched_ex(dt, _LAYOUTS[layout], n, nb,
+                                       _options(SCALE_MAXABS if scale else 0, interleave),
+                                       A.data_ptr(), LU.data_ptr(), piv.data_ptr(),
+                                       info.data_ptr(), s.cuda_stream)
         else:
-            rc = tdls_getrf_batched(dt, _LAYOUTS[layout], n, batch, A.data_ptr(), LU.data_ptr(),
+            rc = tdls_getrf_batched(dt, _LAYOUTS[layout], n, nb, A.data_ptr(), LU.data_ptr(),
                                     piv.data_ptr(), info.data_ptr(), s.cuda_stream)
     if rc != 0:
         raise TdlsError(rc, "tdls_getrf_batched")
     return LU, piv, info
 
 
-def getrs_batched(LU, piv, B, layout: str = "row", out=None, stream=None):
+def getrs_batched(LU, piv, B, layout: str = "row", out=None, stream=None, interleave: int = 1,
+                  batch=None):
     """Solve from factors of getrf_batched: X with A X = B.
 
     LU: [batch, n, n] and piv int32 [batch, n] as returned by getrf_batched
-    (same layout); B: [batch, n, nrhs] ("row") or [batch, nrhs, n] ("col").
-    Returns X shaped like B.  Does not synchronize.
+    (same layout and interleave); B: [batch, n, nrhs] ("row") or [batch,
+    nrhs, n] ("col").  Returns X shaped like B.  Does not synchronize.
     """
     torch = _torch()
-    if layout not in _LAYOUTS:
-        raise ValueError("layout must be 'row' or 'col'")
-    _check_square(torch, LU, "LU")
-    batch, n = LU.shape[0], LU.shape[1]
-    if B.dtype != LU.dtype or not B.is_cuda or B.device != LU.device or not B.is_contiguous():
-        raise ValueError("B must be a contiguous CUDA tensor of LU's dtype and device")
+    _check_pair(torch, LU, B, "LU", "B")
+    nb, n, nrhs = _dims(LU, B, layout, interleave, batch)
     if piv.dtype != torch.int32 or piv.device != LU.device or not piv.is_contiguous() \
-            or tuple(piv.shape) != (batch, n):
-        raise ValueError("piv must be a contiguous int32 [batch, n] tensor on LU's device")
-    if B.dim() != 3 or B.shape[0] != batch:
-        raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
-    nrhs = B.shape[2] if layout == "row" else B.shape[1]
-    if (B.shape[1] if layout == "row" else B.shape[2]) != n:
-        raise ValueError("B does not match n")
+            or tuple(piv.shape) != _piv_shape(LU, n, interleave):
+        raise ValueError("piv must be a contiguous int32 tensor on LU's device, shaped as "
+                         "getrf_batched returns it")
     X = torch.empty_like(B) if out is None else out
     s = stream if stream is not None else torch.cuda.current_stream(LU.device)
+    dt = _dtype_code(torch, LU)
     with torch.cuda.device(LU.device):
-        rc = tdls_getrs_batched(F64 if LU.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
-                                nrhs, batch, LU.data_ptr(), piv.data_ptr(), B.data_ptr(),
-                                X.data_ptr(), s.cuda_stream)
+        if interleave > 1:
+            rc = tdls_getrs_batched_ex(dt, _LAYOUTS[layout], n, nrhs, nb, _options(0, interleave),
+                                       LU.data_ptr(), piv.data_ptr(), B.data_ptr(), X.data_ptr(),
+                                       s.cuda_stream)
+        else:
+            rc = tdls_getrs_batched(dt, _LAYOUTS[layout], n, nrhs, nb, LU.data_ptr(),
+                                    piv.data_ptr(), B.data_ptr(), X.data_ptr(), s.cuda_stream)
     if rc != 0:
         raise TdlsError(rc, "tdls_getrs_batched")
     return X
 
 
-def potrf_batched(A, layout: str = "row", shift: float = 0.0, out=None, stream=None):
+def potrf_batched(A, layout: str = "row", shift: float = 0.0, out=None, stream=None,
+                  interleave: int = 1, batch=None):
     """Cholesky factors of a batch of symmetric matrices: A + shift I = L L^T.
 
     A: [batch, n, n] in ``layout`` (exactly symmetric, else info = -2).
     Returns (L, info): L like A, lower triangular with +0.0 above (all +0.0
-    for a failed system); info int32 [batch] (0, j for the first leading
-    minor that is not positive definite, -2).  Does not synchronize.
+    for a failed system); info int32 [batch] (0; -1 non-finite input; -2;
+    j for the first leading minor that is not positive definite; -3
+    non-finite factor).  ``interleave``: an interleaved batch.  Does not
+    synchronize.
     """
     torch = _torch()
-    if layout not in _LAYOUTS:
-        raise ValueError("layout must be 'row' or 'col'")
-    _check_square(torch, A, "A")
-    batch, n = A.shape[0], A.shape[1]
+    if A.dtype not in (torch.float32, torch.float64) or not A.is_cuda or not A.is_contiguous():
+        raise ValueError("A must be a contiguous float32 or float64 CUDA tensor")
+    nb, n, _ = _dims(A, None, layout, interleave, batch)
     if out is None:
         L = torch.empty_like(A)
-        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+        info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
         L, info = out
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):
-        rc = tdls_potrf_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
-                                batch, shift, A.data_ptr(), L.data_ptr(), info.data_ptr(),
-                                s.cuda_stream)
+        if interleave > 1:
+            rc = tdls_potrf_batched_ex(dt, _LAYOUTS[layout], n, nb, shift,
+                                       _options(0, interleave), A.data_ptr(), L.data_ptr(),
+                                       info.data_ptr(), s.cuda_stream)
+        else:
+            rc = tdls_potrf_batched(dt, _LAYOUTS[layout], n, nb, shift, A.data_ptr(),
+                                    L.data_ptr(), info.data_ptr(), s.cuda_stream)
     if rc != 0:
         raise TdlsError(rc, "tdls_potrf_batched")
     return L, info
 
 
-def posv_batched(A, B, layout: str = "row", shift: float = 0.0, out=None, stream=None):
+def posv_batched(A, B, layout: str = "row", shift: float = 0.0, out=None, stream=None,
+                 interleave: int = 1, batch=None):
     """Solve (A + shift I) X = B by Cholesky for a batch of symmetric
     positive definite systems.  Shapes as for gesv_batched.  Returns (X,
-    info) with potrf_batched's status; a failed system gets X = +0.0."""
+    info) with potrf_batched's status (-1 also for a non-finite entry of B);
+    a failed system gets X = +0.0."""
     torch = _torch()
-    if layout not in _LAYOUTS:
-        raise ValueError("layout must be 'row' or 'col'")
-    _check_square(torch, A, "A")
-    batch, n = A.shape[0], A.shape[1]
-    if B.dtype != A.dtype or not B.is_cuda or B.device != A.device or not B.is_contiguous():
-        raise ValueError("B must be a contiguous CUDA tensor of A's dtype and device")
-    if B.dim() != 3 or B.shape[0] != batch:
-        raise ValueError("B must be [batch, n, nrhs] (row) or [batch, nrhs, n] (col)")
-    nrhs = B.shape[2] if layout == "row" else B.shape[1]
-    if (B.shape[1] if layout == "row" else B.shape[2]) != n:
-        raise ValueError("B does not match n")
+    _check_pair(torch, A, B)
+    nb, n, nrhs = _dims(A, B, layout, interleave, batch)
     if out is None:
         X = torch.empty_like(B)
-        info = torch.empty((batch,), dtype=torch.int32, device=A.device)
+        info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
         X, info = out
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):
-        rc = tdls_posv_batched(F64 if A.dtype == torch.float64 else F32, _LAYOUTS[layout], n,
-                               nrhs, batch, shift, A.data_ptr(), B.data_ptr(), X.data_ptr(),
-                               info.data_ptr(), s.cuda_stream)
+        if interleave > 1:
+            rc = tdls_posv_batched_ex(dt, _LAYOUTS[layout], n, nrhs, nb, shift,
+                                      _options(0, interleave), A.data_ptr(), B.data_ptr(),
+                                      X.data_ptr(), info.data_ptr(), s.cuda_stream)
+        else:
+            rc = tdls_posv_batched(dt, _LAYOUTS[layout], n, nrhs, nb, shift, A.data_ptr(),
+                                   B.data_ptr(), X.data_ptr(), info.data_ptr(), s.cuda_stream)
     if rc != 0:
         raise TdlsError(rc, "tdls_posv_batched")
     return X, info

@@ -93,7 +93,8 @@ __device__ __forceinline__ float sqrt_ieee(float v) { return __builtin_sqrtf(v);
 template <typename Real, int N, int NRHS, int T, bool FACT>
 __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     chol_kernel(int col, int n, int nrhs, int64_t batch, Real shift, const Real* __restrict__ A,
-                const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ info) {
+                const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ info,
+                int64_t ilv) {
   static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
   using S = CholShape<Real, N, NRHS, T>;
   constexpr int R = S::R;
@@ -116,9 +117,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   Real a[R][N];
   Real y[R][NRHS];
   {
-    const Real* As = A + (live ? sys : 0) * (int64_t)n * n;
-    const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
-    if (n == N && nrhs == NRHS) {
+    const Real* As = A + sys_start(live ? sys : 0, ilv, (int64_t)n * n);
+    const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
+    if (n == N && nrhs == NRHS && ilv == 1) {
       // the kernel's own size: compile-time offsets from one base per row
       auto load_exact = [&](auto colc) {
         constexpr bool COL = decltype(colc)::value;
@@ -154,13 +155,14 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         sfor<0, N>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           a[K][c] = (q == c) ? Real(1) : Real(0);
-          if (qrow && c < n) a[K][c] = As[col ? (int64_t)c * n + qq : (int64_t)qq * n + c];
+          if (qrow && c < n) a[K][c] = As[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
         });
         sfor<0, NRHS>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           y[K][j] = Real(0);
           if constexpr (!FACT)
-            if (qrow && j < nrhs) y[K][j] = Bs[col ? (int64_t)j * n + qq : (int64_t)qq * nrhs + j];
+            if (qrow && j < nrhs)
+              y[K][j] = Bs[(col ? (int64_t)j * n + qq : (int64_t)qq * nrhs + j) * ilv];
         });
       });
     }
@@ -317,7 +319,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
     const bool failed = status != 0;
     if (live) {
-      Real* Ls = X + sys * ((int64_t)n * n);
+      Real* Ls = X + sys_start(sys, ilv, (int64_t)n * n);
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
@@ -326,15 +328,16 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             constexpr bool COL = decltype(colc)::value;
             constexpr bool EXACT = decltype(exactc)::value;
             const int64_t ld = EXACT ? N : n;
-            Real* rowp = Ls + (COL ? (int64_t)q : (int64_t)q * ld);
+            const int64_t es = EXACT ? 1 : ilv;  // element stride
+            Real* rowp = Ls + (COL ? (int64_t)q : (int64_t)q * ld) * es;
             sfor<0, N>([&](auto cc) {
               constexpr int c = decltype(cc)::value;
               const Real v = (failed || c > q) ? Real(0) : a[K][c];
-              if (EXACT || c < n) rowp[COL ? c * ld : c] = v;
+              if (EXACT || c < n) rowp[(COL ? c * ld : c) * es] = v;
               if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
             });
           };
-          if (n == N) {
+          if (n == N && ilv == 1) {
             if (col)
               store_row(std::true_type{}, std::true_type{});
             else
@@ -356,7 +359,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // ---- L^T x = y with the solver of the LU path: U = L^T, so lane c
       // writes L(c, q) into row q of the triangular store for every q <= c
       xbad = upper_solve_store<Real, N, NRHS, T>(
-          sq, tx, (int)(g * T), live, failed, live ? sys : 0, n, nrhs, col, X,
+          sq, tx, (int)(g * T), live, failed, live ? sys : 0, n, nrhs, col, ilv, X,
           [&](Real* yt) {
             sfor<0, R>([&](auto Kc) {
               constexpr int K = decltype(Kc)::value;
@@ -498,7 +501,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       });
       xbad = group_any<T>(bad, gb);
       if (live) {
-        Real* Xs = X + sys * ((int64_t)n * nrhs);
+        Real* Xs = X + sys_start(sys, ilv, (int64_t)n * nrhs);
         const bool zero = failed || xbad;
         sfor<0, QR>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
@@ -509,9 +512,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             if (q < n && r < nrhs) {
               const Real v = zero ? Real(0) : xr[m][jj];
               if (col)
-                Xs[(int64_t)r * n + q] = v;
+                Xs[((int64_t)r * n + q) * ilv] = v;
               else
-                Xs[(int64_t)q * nrhs + r] = v;
+                Xs[((int64_t)q * nrhs + r) * ilv] = v;
             }
           });
         });

@@ -35,7 +35,7 @@ static int launch_panel(const LaunchPlan& p, const void* A, const void* B, void*
   hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB, FACT>), dim3((unsigned)p.grid),
                      dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                      p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),
-                     static_cast<Real*>(X), piv, info, p.flags);
+                     static_cast<Real*>(X), piv, info, p.flags, p.interleave);
   return (int)hipGetLastError();
 }
 
@@ -48,7 +48,7 @@ static int launch_getrs(const LaunchPlan& p, const void* LU, const void* B, void
   hipLaunchKernelGGL((getrs_kernel<Real, N, NRHS, T>), dim3((unsigned)p.grid),
                      dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                      p.batch, static_cast<const Real*>(LU), piv, static_cast<const Real*>(B),
-                     static_cast<Real*>(X));
+                     static_cast<Real*>(X), p.interleave);
   return (int)hipGetLastError();
 }
 
@@ -66,7 +66,7 @@ static int launch_chol(const LaunchPlan& p, const void* A, const void* B, void* 
     hipLaunchKernelGGL((chol_kernel<Real, N, NRHS, T, FACT>), dim3((unsigned)p.grid),
                        dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                        p.batch, (Real)p.shift, static_cast<const Real*>(A),
-                       static_cast<const Real*>(B), static_cast<Real*>(X), info);
+                       static_cast<const Real*>(B), static_cast<Real*>(X), info, p.interleave);
     return (int)hipGetLastError();
   }
 }

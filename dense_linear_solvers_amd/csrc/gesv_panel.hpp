@@ -254,6 +254,15 @@ __device__ __forceinline__ bool group_any(bool v, int gbase) {
 __device__ __forceinline__ bool not_finite(double v) { return !__builtin_isfinite(v); }
 __device__ __forceinline__ bool not_finite(float v) { return !__builtin_isfinite(v); }
 
+// Start of system s in a batch of systems of E elements each, stored with W
+// systems interleaved element by element (the single strided form of the
+// TDLS page, section Residency: W = 1 one system after another, W = batch
+// a structure of arrays, other W blocks of W systems): element e of system
+// s lives at sys_start(s) + e * W.
+__device__ __forceinline__ int64_t sys_start(int64_t s, int64_t W, int64_t E) {
+  return W == 1 ? s * E : (s / W) * W * E + s % W;
+}
+
 __device__ __forceinline__ uint32_t hi_word(double v) {
   return (uint32_t)(__builtin_bit_cast(uint64_t, v) >> 32);
 }
@@ -291,13 +300,13 @@ __device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2;
 template <typename Real, int N, int NRHS, int T, typename WR, typename WU>
 __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, bool live,
                                                   bool failed, int64_t sys, int n, int nrhs,
-                                                  int col, Real* X, WR&& write_rhs,
+                                                  int col, int64_t ilv, Real* X, WR&& write_rhs,
                                                   WU&& write_u) {
   constexpr int R = (N + T - 1) / T;
   bool xbad = false;
   write_rhs(ut);
   wave_sync_lds();
-  Real* Xs = X + sys * ((int64_t)n * nrhs);
+  Real* Xs = X + sys_start(sys, ilv, (int64_t)n * nrhs);
   // layout of the solve (see below): one right-hand side by slots; several
   // by column classes and row phases
   constexpr int NJ = NRHS < T ? NRHS : T;
@@ -377,7 +386,7 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
-        if (q < n) Xs[q] = zero ? Real(0) : xr[K];   // one column: same address in both layouts
+        if (q < n) Xs[q * ilv] = zero ? Real(0) : xr[K];   // one column: same address in both layouts
       });
     }
   } else {
@@ -438,9 +447,9 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
           if (q < n && j < nrhs) {
             const Real v = zero ? Real(0) : xr[m][jj];
             if (col)
-              Xs[(int64_t)j * n + q] = v;
+              Xs[((int64_t)j * n + q) * ilv] = v;
             else
-              Xs[(int64_t)q * nrhs + j] = v;
+              Xs[((int64_t)q * nrhs + j) * ilv] = v;
           }
         });
       });
@@ -456,7 +465,7 @@ template <typename Real, int N, int NRHS, int T, int B, bool FACT = false>
 __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     gesv_panel_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ A,
                       const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ piv,
-                      int32_t* __restrict__ info, uint32_t flags) {
+                      int32_t* __restrict__ info, uint32_t flags, int64_t ilv) {
   static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
   static_assert(N > B, "the first panel has trailing columns (input check)");
   using S = PanelShape<Real, N, NRHS, T, B>;
@@ -493,9 +502,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   // kernel's shape every address is a per-slot base plus a compile-time
   // offset and every load lands directly in its row register.
   {
-    const Real* As = A + (live ? sys : 0) * (int64_t)n * n;
-    const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
-    if (n == N && nrhs == NRHS) {
+    const Real* As = A + sys_start(live ? sys : 0, ilv, (int64_t)n * n);
+    const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
+    if (n == N && nrhs == NRHS && ilv == 1) {
       // Loads are issued column by column over the slots, so the first
       // pivot search waits only for the first column to arrive while the
       // rest of the tile streams in behind it.
@@ -538,10 +547,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         const int q = tx + K * T;
         const bool qrow = live && q < n;
         const int qq = qrow ? q : 0;
-        const int64_t cs = col ? n : 1;          // element stride between columns
-        const Real* ar = As + (col ? qq : (int64_t)qq * n);
-        const int64_t js = col ? n : 1;
-        const Real* br = Bs + (col ? qq : (int64_t)qq * nrhs);
+        const int64_t cs = (col ? n : 1) * ilv;  // element stride between columns
+        const Real* ar = As + (col ? qq : (int64_t)qq * n) * ilv;
+        const int64_t js = (col ? n : 1) * ilv;
+        const Real* br = Bs + (col ? qq : (int64_t)qq * nrhs) * ilv;
         // identity block, then the stored entries; the scheduling barriers
         // keep few loads (and their 64-bit addresses) in flight at a time
         sfor<0, N>([&](auto cc) {
@@ -912,8 +921,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
     const bool failed = status != 0;
     if (live) {
-      Real* LUs = X + sys * ((int64_t)n * n);
-      int32_t* Ps = piv + sys * (int64_t)n;
+      Real* LUs = X + sys_start(sys, ilv, (int64_t)n * n);
+      int32_t* Ps = piv + sys_start(sys, ilv, n);
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = lab[K];
@@ -926,14 +935,15 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             constexpr bool COL = decltype(colc)::value;
             constexpr bool EXACT = decltype(exactc)::value;
             const int64_t ld = EXACT ? N : n;
-            Real* rowp = LUs + (COL ? (int64_t)q : (int64_t)q * ld);
+            const int64_t es = EXACT ? 1 : ilv;  // element stride
+            Real* rowp = LUs + (COL ? (int64_t)q : (int64_t)q * ld) * es;
             sfor<0, N>([&](auto cc) {
               constexpr int c = decltype(cc)::value;
-              if (EXACT || c < n) rowp[COL ? c * ld : c] = failed ? Real(0) : a[K][c];
+              if (EXACT || c < n) rowp[(COL ? c * ld : c) * es] = failed ? Real(0) : a[K][c];
               if constexpr (c % 8 == 7) __builtin_amdgcn_sched_barrier(0);
             });
           };
-          if (n == N) {
+          if (n == N && ilv == 1) {
             if (col)
               store_row(std::true_type{}, std::true_type{});
             else
@@ -946,7 +956,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           }
         }
         const int qf = tx + K * T;
-        if (qf < n) Ps[qf] = failed ? -1 : pv[K];
+        if (qf < n) Ps[qf * ilv] = failed ? -1 : pv[K];
       });
       if (tx == 0) info[sys] = status;
     }
@@ -955,10 +965,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   // ---- back substitution (see upper_solve_store): every row, whatever lane
   // holds it, stores its right-hand sides and then its U entries (columns
   // from its position on) by position
-  int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
+  int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
   wave_sync_lds();  // the last records have been read
   const bool xbad = upper_solve_store<Real, N, NRHS, T>(
-      rec, tx, gbase, live, status != 0 || nf != 0, live ? sys : 0, n, nrhs, col, X,
+      rec, tx, gbase, live, status != 0 || nf != 0, live ? sys : 0, n, nrhs, col, ilv, X,
       [&](Real* yt) {
         sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
@@ -993,7 +1003,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     sfor<0, R>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
       const int q = tx + K * T;
-      if (q < n) Ps[q] = failed ? -1 : pv[K];
+      if (q < n) Ps[q * ilv] = failed ? -1 : pv[K];
     });
     if (tx == 0) info[sys] = status;
   }

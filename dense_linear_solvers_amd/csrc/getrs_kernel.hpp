@@ -41,7 +41,7 @@ template <typename Real, int N, int NRHS, int T>
 __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     getrs_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ LU,
                  const int32_t* __restrict__ piv, const Real* __restrict__ Bm,
-                 Real* __restrict__ X) {
+                 Real* __restrict__ X, int64_t ilv) {
   using S = GetrsShape<Real, N, NRHS, T>;
   constexpr int R = S::R;
   constexpr int G = S::G;
@@ -62,11 +62,11 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   // ---- the swap sequence to LDS (the identity past n and for groups past
   // the batch), then the source row of each position: walking the swaps
   // from the last to the first maps a position to the row it receives.
-  const int32_t* Ps = piv + (live ? sys : 0) * (int64_t)n;
+  const int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
   sfor<0, R>([&](auto Kc) {
     constexpr int K = decltype(Kc)::value;
     const int q = tx + K * T;
-    if (q < N) pl[q] = (live && q < n) ? Ps[q] : q;
+    if (q < N) pl[q] = (live && q < n) ? Ps[q * ilv] : q;
   });
   wave_sync_lds();
   const bool failed = pl[0] < 0;   // a failed factorization: every pivot -1
@@ -88,10 +88,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   Real a[R][N];
   Real y[R][NRHS];
   {
-    const Real* Ls = LU + (live ? sys : 0) * (int64_t)n * n;
-    const Real* Bs = Bm + (live ? sys : 0) * (int64_t)n * nrhs;
+    const Real* Ls = LU + sys_start(live ? sys : 0, ilv, (int64_t)n * n);
+    const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
     auto src_row = [&](int K) { return src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]); };
-    if (n == N && nrhs == NRHS) {
+    if (n == N && nrhs == NRHS && ilv == 1) {
       // the kernel's own size: compile-time offsets from one base per row
       // (a row-major row is one run of vector loads)
       auto load_exact = [&](auto colc) {
@@ -127,12 +127,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         sfor<0, N>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           a[K][c] = (q == c) ? Real(1) : Real(0);
-          if (qrow && c < n) a[K][c] = Ls[col ? (int64_t)c * n + qq : (int64_t)qq * n + c];
+          if (qrow && c < n) a[K][c] = Ls[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
         });
         sfor<0, NRHS>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           y[K][j] = Real(0);
-          if (qrow && j < nrhs) y[K][j] = Bs[col ? (int64_t)j * n + sr : (int64_t)sr * nrhs + j];
+          if (qrow && j < nrhs)
+            y[K][j] = Bs[(col ? (int64_t)j * n + sr : (int64_t)sr * nrhs + j) * ilv];
         });
       });
     }
@@ -202,7 +203,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
 
   // ---- store X (all +0.0 when the factorization failed)
   if (live) {
-    Real* Xs = X + sys * ((int64_t)n * nrhs);
+    Real* Xs = X + sys_start(sys, ilv, (int64_t)n * nrhs);
     sfor<0, R>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
       const int q = tx + K * T;
@@ -212,9 +213,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           if (j < nrhs) {
             const Real v = failed ? Real(0) : xr[K][j];
             if (col)
-              Xs[(int64_t)j * n + q] = v;
+              Xs[((int64_t)j * n + q) * ilv] = v;
             else
-              Xs[(int64_t)q * nrhs + j] = v;
+              Xs[((int64_t)q * nrhs + j) * ilv] = v;
           }
         });
       }

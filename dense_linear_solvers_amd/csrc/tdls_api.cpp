@@ -94,6 +94,7 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   if (p->grid > 0x7fffffffLL) return -5;
   p->shift = 0.0;
   p->flags = 0;
+  p->interleave = 1;
   p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, T)
                  : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, NRHS, T, is64)
                                                      : gesv_lds_bytes(N, NRHS, T, is64);
@@ -128,11 +129,12 @@ int launch(const LaunchPlan& p, const void* in0, const void* in1, void* out, int
 }
 
 // Options of the *_ex calls: flags allowed for the operation, reserved
-// field zero, systems one after another.
-bool bad_options(const tdls_options* opt, uint32_t allowed_flags) {
+// field zero, an interleave of 0 or 1 (systems one after another) or of 2 ..
+// batch systems.
+bool bad_options(const tdls_options* opt, uint32_t allowed_flags, int64_t batch) {
   if (opt == nullptr) return false;
   if ((opt->flags & ~allowed_flags) != 0 || opt->reserved != 0) return true;
-  return opt->interleave != 0 && opt->interleave != 1;
+  return opt->interleave < 0 || (opt->interleave > 1 && batch > 0 && opt->interleave > batch);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -187,21 +189,48 @@ int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nr
 namespace tdls {
 namespace {
 
-// The pointer checks of gesv; `po` is added to the code of each pointer
-// argument (1 when an options argument comes before them).
+// What the *_ex calls add: option flags, the batch interleave W (element e
+// of system s at (s / W) W E + (s % W) + e W for systems of E elements), and
+// `po`, the shift of the pointer arguments' numbers (1 after an options
+// argument).
+struct Extra {
+  uint32_t flags = 0;
+  int64_t ilv = 1;
+  int po = 0;
+};
+
+Extra extra_of(const tdls_options* opt) {
+  Extra x;
+  x.po = 1;
+  if (opt != nullptr) {
+    x.flags = opt->flags;
+    x.ilv = opt->interleave <= 1 ? 1 : opt->interleave;
+  }
+  return x;
+}
+
+// Bytes spanned by a buffer of `batch` systems of E elements under
+// interleave W: whole blocks of W systems.
+size_t span(int64_t batch, int64_t W, int64_t E, size_t es) {
+  const int64_t blocks = (batch + W - 1) / W;
+  return (size_t)blocks * (size_t)W * (size_t)E * es;
+}
+
 int gesv_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
-              uint32_t flags, int po, const void* A, const void* B, void* X, int32_t* piv,
+              const Extra& x, const void* A, const void* B, void* X, int32_t* piv,
               int32_t* info, hipStream_t stream) {
   tdls::LaunchPlan p;
   int rc = tdls::make_plan(tdls::kOpGesv, (int)dtype, (int)layout, n, nrhs, batch, &p);
   if (rc != 0) return rc;
   if (batch == 0) return TDLS_SUCCESS;  // nothing to read or write, nothing launched
-  p.flags = flags;
+  p.flags = x.flags;
+  p.interleave = x.ilv;
+  const int po = x.po;
 
   const size_t es = dtype == TDLS_F64 ? 8 : 4;
-  const size_t bytesA = (size_t)batch * n * n * es;
-  const size_t bytesB = (size_t)batch * n * nrhs * es;
-  const size_t bytesP = (size_t)batch * n * 4;
+  const size_t bytesA = span(batch, x.ilv, (int64_t)n * n, es);
+  const size_t bytesB = span(batch, x.ilv, (int64_t)n * nrhs, es);
+  const size_t bytesP = span(batch, x.ilv, n, 4);
   const size_t bytesI = (size_t)batch * 4;
   if (A == nullptr || tdls::misaligned(A, es)) return -6 - po;
   if (B == nullptr || tdls::misaligned(B, es)) return -7 - po;
@@ -218,19 +247,20 @@ int gesv_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t bat
   return tdls::launch(p, A, B, X, piv, info, stream);
 }
 
-int getrf_call(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, uint32_t flags,
-               int po, const void* A, void* LU, int32_t* piv, int32_t* info,
-               hipStream_t stream) {
+int getrf_call(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, const Extra& x,
+               const void* A, void* LU, int32_t* piv, int32_t* info, hipStream_t stream) {
   tdls::LaunchPlan p;
   int rc = tdls::make_plan(tdls::kOpGetrf, (int)dtype, (int)layout, n, 1, batch, &p);
   if (rc == -5) return -4;   // batch is argument 4 here
   if (rc != 0) return rc;
   if (batch == 0) return TDLS_SUCCESS;
-  p.flags = flags;
+  p.flags = x.flags;
+  p.interleave = x.ilv;
+  const int po = x.po;
 
   const size_t es = dtype == TDLS_F64 ? 8 : 4;
-  const size_t bytesA = (size_t)batch * n * n * es;
-  const size_t bytesP = (size_t)batch * n * 4;
+  const size_t bytesA = span(batch, x.ilv, (int64_t)n * n, es);
+  const size_t bytesP = span(batch, x.ilv, n, 4);
   const size_t bytesI = (size_t)batch * 4;
   if (A == nullptr || tdls::misaligned(A, es)) return -5 - po;
   if (LU == nullptr || tdls::misaligned(LU, es) || tdls::overlaps(LU, bytesA, A, bytesA))
@@ -244,6 +274,80 @@ int getrf_call(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, uint3
   return tdls::launch(p, A, nullptr, LU, piv, info, stream);
 }
 
+int getrs_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+               const Extra& x, const void* LU, const int32_t* piv, const void* B, void* X,
+               hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpGetrs, (int)dtype, (int)layout, n, nrhs, batch, &p);
+  if (rc != 0) return rc;
+  if (batch == 0) return TDLS_SUCCESS;
+  p.interleave = x.ilv;
+  const int po = x.po;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesLU = span(batch, x.ilv, (int64_t)n * n, es);
+  const size_t bytesP = span(batch, x.ilv, n, 4);
+  const size_t bytesB = span(batch, x.ilv, (int64_t)n * nrhs, es);
+  if (LU == nullptr || tdls::misaligned(LU, es)) return -6 - po;
+  if (piv == nullptr || tdls::misaligned(piv, 4)) return -7 - po;
+  if (B == nullptr || tdls::misaligned(B, es)) return -8 - po;
+  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, LU, bytesLU) ||
+      tdls::overlaps(X, bytesB, piv, bytesP) || tdls::overlaps(X, bytesB, B, bytesB))
+    return -9 - po;
+  return tdls::launch(p, LU, B, X, const_cast<int32_t*>(piv), nullptr, stream);
+}
+
+int potrf_call(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, double shift,
+               const Extra& x, const void* A, void* L, int32_t* info, hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpPotrf, (int)dtype, (int)layout, n, 1, batch, &p);
+  if (rc == -5) return -4;   // batch is argument 4 here
+  if (rc != 0) return rc;
+  if (!std::isfinite(shift)) return -5;
+  if (batch == 0) return TDLS_SUCCESS;
+  p.shift = shift;
+  p.interleave = x.ilv;
+  const int po = x.po;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesA = span(batch, x.ilv, (int64_t)n * n, es);
+  const size_t bytesI = (size_t)batch * 4;
+  if (A == nullptr || tdls::misaligned(A, es)) return -6 - po;
+  if (L == nullptr || tdls::misaligned(L, es) || tdls::overlaps(L, bytesA, A, bytesA))
+    return -7 - po;
+  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
+      tdls::overlaps(info, bytesI, L, bytesA))
+    return -8 - po;
+  return tdls::launch(p, A, nullptr, L, nullptr, info, stream);
+}
+
+int posv_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+              double shift, const Extra& x, const void* A, const void* B, void* X,
+              int32_t* info, hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpPosv, (int)dtype, (int)layout, n, nrhs, batch, &p);
+  if (rc != 0) return rc;
+  if (!std::isfinite(shift)) return -6;
+  if (batch == 0) return TDLS_SUCCESS;
+  p.shift = shift;
+  p.interleave = x.ilv;
+  const int po = x.po;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesA = span(batch, x.ilv, (int64_t)n * n, es);
+  const size_t bytesB = span(batch, x.ilv, (int64_t)n * nrhs, es);
+  const size_t bytesI = (size_t)batch * 4;
+  if (A == nullptr || tdls::misaligned(A, es)) return -7 - po;
+  if (B == nullptr || tdls::misaligned(B, es)) return -8 - po;
+  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, A, bytesA) ||
+      tdls::overlaps(X, bytesB, B, bytesB))
+    return -9 - po;
+  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
+      tdls::overlaps(info, bytesI, B, bytesB) || tdls::overlaps(info, bytesI, X, bytesB))
+    return -10 - po;
+  return tdls::launch(p, A, B, X, nullptr, info, stream);
+}
+
 }  // namespace
 }  // namespace tdls
 
@@ -252,7 +356,8 @@ extern "C" {
 int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                       const void* A, const void* B, void* X, int32_t* piv, int32_t* info,
                       hipStream_t stream) {
-  return tdls::gesv_call(dtype, layout, n, nrhs, batch, 0u, 0, A, B, X, piv, info, stream);
+  return tdls::gesv_call(dtype, layout, n, nrhs, batch, tdls::Extra(), A, B, X, piv, info,
+                         stream);
 }
 
 int tdls_gesv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
@@ -260,15 +365,15 @@ int tdls_gesv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, 
                          int32_t* piv, int32_t* info, hipStream_t stream) {
   const int rc = tdls::check_scalars((int)dtype, (int)layout, n, nrhs, batch);
   if (rc != 0) return rc;
-  if (tdls::bad_options(opt, TDLS_SCALE_MAXABS)) return -6;
-  return tdls::gesv_call(dtype, layout, n, nrhs, batch, opt ? opt->flags : 0u, 1, A, B, X, piv,
+  if (tdls::bad_options(opt, TDLS_SCALE_MAXABS, batch)) return -6;
+  return tdls::gesv_call(dtype, layout, n, nrhs, batch, tdls::extra_of(opt), A, B, X, piv,
                          info, stream);
 }
 
 int tdls_getrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
                        const void* A, void* LU, int32_t* piv, int32_t* info,
                        hipStream_t stream) {
-  return tdls::getrf_call(dtype, layout, n, batch, 0u, 0, A, LU, piv, info, stream);
+  return tdls::getrf_call(dtype, layout, n, batch, tdls::Extra(), A, LU, piv, info, stream);
 }
 
 int tdls_getrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
@@ -276,76 +381,59 @@ int tdls_getrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t b
                           int32_t* info, hipStream_t stream) {
   const int rc = tdls::check_scalars((int)dtype, (int)layout, n, 1, batch);
   if (rc != 0) return rc == -5 ? -4 : rc;
-  if (tdls::bad_options(opt, TDLS_SCALE_MAXABS)) return -5;
-  return tdls::getrf_call(dtype, layout, n, batch, opt ? opt->flags : 0u, 1, A, LU, piv, info,
+  if (tdls::bad_options(opt, TDLS_SCALE_MAXABS, batch)) return -5;
+  return tdls::getrf_call(dtype, layout, n, batch, tdls::extra_of(opt), A, LU, piv, info,
                           stream);
 }
 
 int tdls_getrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                        const void* LU, const int32_t* piv, const void* B, void* X,
                        hipStream_t stream) {
-  tdls::LaunchPlan p;
-  int rc = tdls::make_plan(tdls::kOpGetrs, (int)dtype, (int)layout, n, nrhs, batch, &p);
-  if (rc != 0) return rc;
-  if (batch == 0) return TDLS_SUCCESS;
+  return tdls::getrs_call(dtype, layout, n, nrhs, batch, tdls::Extra(), LU, piv, B, X, stream);
+}
 
-  const size_t es = dtype == TDLS_F64 ? 8 : 4;
-  const size_t bytesLU = (size_t)batch * n * n * es;
-  const size_t bytesP = (size_t)batch * n * 4;
-  const size_t bytesB = (size_t)batch * n * nrhs * es;
-  if (LU == nullptr || tdls::misaligned(LU, es)) return -6;
-  if (piv == nullptr || tdls::misaligned(piv, 4)) return -7;
-  if (B == nullptr || tdls::misaligned(B, es)) return -8;
-  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, LU, bytesLU) ||
-      tdls::overlaps(X, bytesB, piv, bytesP) || tdls::overlaps(X, bytesB, B, bytesB))
-    return -9;
-  return tdls::launch(p, LU, B, X, const_cast<int32_t*>(piv), nullptr, stream);
+int tdls_getrs_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                          const tdls_options* opt, const void* LU, const int32_t* piv,
+                          const void* B, void* X, hipStream_t stream) {
+  const int rc = tdls::check_scalars((int)dtype, (int)layout, n, nrhs, batch);
+  if (rc != 0) return rc;
+  if (tdls::bad_options(opt, 0u, batch)) return -6;
+  return tdls::getrs_call(dtype, layout, n, nrhs, batch, tdls::extra_of(opt), LU, piv, B, X,
+                          stream);
 }
 
 int tdls_potrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, double shift,
                        const void* A, void* L, int32_t* info, hipStream_t stream) {
-  tdls::LaunchPlan p;
-  int rc = tdls::make_plan(tdls::kOpPotrf, (int)dtype, (int)layout, n, 1, batch, &p);
-  if (rc == -5) return -4;   // batch is argument 4 here
-  if (rc != 0) return rc;
-  if (!std::isfinite(shift)) return -5;
-  if (batch == 0) return TDLS_SUCCESS;
-  p.shift = shift;
+  return tdls::potrf_call(dtype, layout, n, batch, shift, tdls::Extra(), A, L, info, stream);
+}
 
-  const size_t es = dtype == TDLS_F64 ? 8 : 4;
-  const size_t bytesA = (size_t)batch * n * n * es;
-  const size_t bytesI = (size_t)batch * 4;
-  if (A == nullptr || tdls::misaligned(A, es)) return -6;
-  if (L == nullptr || tdls::misaligned(L, es) || tdls::overlaps(L, bytesA, A, bytesA)) return -7;
-  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
-      tdls::overlaps(info, bytesI, L, bytesA))
-    return -8;
-  return tdls::launch(p, A, nullptr, L, nullptr, info, stream);
+int tdls_potrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                          double shift, const tdls_options* opt, const void* A, void* L,
+                          int32_t* info, hipStream_t stream) {
+  const int rc = tdls::check_scalars((int)dtype, (int)layout, n, 1, batch);
+  if (rc != 0) return rc == -5 ? -4 : rc;
+  if (!std::isfinite(shift)) return -5;
+  if (tdls::bad_options(opt, 0u, batch)) return -6;
+  return tdls::potrf_call(dtype, layout, n, batch, shift, tdls::extra_of(opt), A, L, info,
+                          stream);
 }
 
 int tdls_posv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                       double shift, const void* A, const void* B, void* X, int32_t* info,
                       hipStream_t stream) {
-  tdls::LaunchPlan p;
-  int rc = tdls::make_plan(tdls::kOpPosv, (int)dtype, (int)layout, n, nrhs, batch, &p);
+  return tdls::posv_call(dtype, layout, n, nrhs, batch, shift, tdls::Extra(), A, B, X, info,
+                         stream);
+}
+
+int tdls_posv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                         double shift, const tdls_options* opt, const void* A, const void* B,
+                         void* X, int32_t* info, hipStream_t stream) {
+  const int rc = tdls::check_scalars((int)dtype, (int)layout, n, nrhs, batch);
   if (rc != 0) return rc;
   if (!std::isfinite(shift)) return -6;
-  if (batch == 0) return TDLS_SUCCESS;
-  p.shift = shift;
-
-  const size_t es = dtype == TDLS_F64 ? 8 : 4;
-  const size_t bytesA = (size_t)batch * n * n * es;
-  const size_t bytesB = (size_t)batch * n * nrhs * es;
-  const size_t bytesI = (size_t)batch * 4;
-  if (A == nullptr || tdls::misaligned(A, es)) return -7;
-  if (B == nullptr || tdls::misaligned(B, es)) return -8;
-  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, A, bytesA) ||
-      tdls::overlaps(X, bytesB, B, bytesB))
-    return -9;
-  if (info == nullptr || tdls::misaligned(info, 4) || tdls::overlaps(info, bytesI, A, bytesA) ||
-      tdls::overlaps(info, bytesI, B, bytesB) || tdls::overlaps(info, bytesI, X, bytesB))
-    return -10;
-  return tdls::launch(p, A, B, X, nullptr, info, stream);
+  if (tdls::bad_options(opt, 0u, batch)) return -7;
+  return tdls::posv_call(dtype, layout, n, nrhs, batch, shift, tdls::extra_of(opt), A, B, X,
+                         info, stream);
 }
 
 const char* tdls_strerror(int code) {
@@ -356,8 +444,8 @@ const char* tdls_strerror(int code) {
     case -3: return "argument 3 is invalid (n outside 1..64, or layout for tdls_plan_op)";
     case -4: return "argument 4 is invalid (nrhs outside 1..8; batch for getrf; n for plan_op)";
     case -5: return "argument 5 is invalid (batch; A for getrf; shift for potrf; nrhs for plan_op; options for getrf_ex)";
-    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; shift for posv; batch for plan_op; options for gesv_ex)";
-    case -7: return "argument 7 is invalid (null, misaligned or overlapping buffer)";
+    case -6: return "argument 6 is invalid (null, misaligned or overlapping buffer; shift for posv; batch for plan_op; options for gesv_ex, getrs_ex, potrf_ex)";
+    case -7: return "argument 7 is invalid (null, misaligned or overlapping buffer; options for posv_ex)";
     case -8: return "argument 8 is invalid (null, misaligned or overlapping buffer)";
     case -9: return "argument 9 is invalid (null, misaligned or overlapping buffer)";
     case -10: return "argument 10 is invalid (null, misaligned or overlapping buffer)";

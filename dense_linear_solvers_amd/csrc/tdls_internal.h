@@ -57,6 +57,7 @@ struct LaunchPlan {
   int64_t batch;
   double shift;       // Cholesky: explicit diagonal shift (0 otherwise)
   uint32_t flags;     // kFlag* options of the call
+  int64_t interleave; // systems interleaved element by element (1: one after another)
   int64_t systems_per_block;
   int64_t grid;
   int threads_per_block;

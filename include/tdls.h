@@ -266,10 +266,25 @@ int tdls_posv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int
 typedef struct tdls_options {
   uint32_t flags;     /* 0, or TDLS_SCALE_MAXABS (gesv and getrf only) */
   uint32_t reserved;  /* must be 0 */
-  int64_t interleave; /* how systems are laid out: 0 or 1, one after another
-                         (the layout of the plain calls); other values are
-                         rejected */
+  int64_t interleave; /* W: how the systems of the batch are laid out */
 } tdls_options;
+
+/*
+ * Batch interleave W of the *_ex calls ("solver_static.hpp File Reference",
+ * section Residency: one strided form, element e of a system at
+ * base[e * stride], covers arrays of structures (stride 1), structures of
+ * arrays (stride = batch) and arrays of structures of arrays (stride = W)).
+ * For a per-system array of E elements (A, LU, L: E = n*n in the layout
+ * flag's order; B, X: E = n*nrhs; piv: E = n), element e of system s lives
+ * at
+ *     (s / W) * W * E + (s % W) + e * W.
+ * W = 0 or 1: systems one after another, as in the plain calls.  W = batch:
+ * a structure of arrays.  1 < W < batch: blocks of W systems; when batch
+ * is not a multiple of W the last block still spans W * E elements (its
+ * missing systems are neither read nor written).  W must not exceed batch
+ * (for batch > 0).  info stays one int32 per system, in order.  Results
+ * are bitwise those of the plain calls on the same systems.
+ */
 
 /*
  * tdls_gesv_batched with options (opt may be NULL: no options).
@@ -283,8 +298,9 @@ typedef struct tdls_options {
  * is decided on the scaled system (a non-finite input still gives -1).
  *
  * Arguments: [1]..[5] as for tdls_gesv_batched, [6] opt (-6 for an unknown
- * flag, a nonzero reserved field or an unsupported interleave), [7] A,
- * [8] B, [9] X, [10] piv, [11] info, stream.
+ * flag, a nonzero reserved field, or an interleave below 0 or above batch),
+ * [7] A, [8] B, [9] X, [10] piv, [11] info, stream.  Buffers span the
+ * interleaved extent (see tdls_options).
  */
 int tdls_gesv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
                          const tdls_options* opt, const void* A, const void* B, void* X,
@@ -302,6 +318,39 @@ int tdls_gesv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, 
 int tdls_getrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
                           const tdls_options* opt, const void* A, void* LU, int32_t* piv,
                           int32_t* info, hipStream_t stream);
+
+/*
+ * tdls_getrs_batched with options (opt may be NULL; no flags): the batch
+ * interleave applies to LU, piv, B and X alike.
+ *
+ * Arguments: [1]..[5] as for tdls_getrs_batched, [6] opt, [7] LU, [8] piv,
+ * [9] B, [10] X, stream.
+ */
+int tdls_getrs_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                          const tdls_options* opt, const void* LU, const int32_t* piv,
+                          const void* B, void* X, hipStream_t stream);
+
+/*
+ * tdls_potrf_batched with options (opt may be NULL; no flags): the batch
+ * interleave applies to A and L.
+ *
+ * Arguments: [1]..[5] as for tdls_potrf_batched, [6] opt, [7] A, [8] L,
+ * [9] info, stream.
+ */
+int tdls_potrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
+                          double shift, const tdls_options* opt, const void* A, void* L,
+                          int32_t* info, hipStream_t stream);
+
+/*
+ * tdls_posv_batched with options (opt may be NULL; no flags): the batch
+ * interleave applies to A, B and X.
+ *
+ * Arguments: [1]..[6] as for tdls_posv_batched, [7] opt, [8] A, [9] B,
+ * [10] X, [11] info, stream.
+ */
+int tdls_posv_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                         double shift, const tdls_options* opt, const void* A, const void* B,
+                         void* X, int32_t* info, hipStream_t stream);
 
 /*
  * tdls_plan_gesv for any operation: [1] op, then the scalar arguments of

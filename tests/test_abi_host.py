@@ -245,7 +245,7 @@ def test_options_validation_before_launch(lib):
     assert tdls.tdls_gesv_batched_ex(1, 0, n, nrhs, -2, Opt(8, 0, 1), a, b, x, pv, inf, 0) == -5
     assert g(Opt(2, 0, 1), a, b, x, pv, inf) == -6      # unknown flag
     assert g(Opt(1, 7, 1), a, b, x, pv, inf) == -6      # reserved field
-    assert g(Opt(1, 0, 5), a, b, x, pv, inf) == -6      # interleave not supported here
+    assert g(Opt(1, 0, 11), a, b, x, pv, inf) == -6     # interleave above batch
     assert g(Opt(1, 0, -1), a, b, x, pv, inf) == -6
     assert g(None, 0, b, x, pv, inf) == -7
     assert g(Opt(1, 0, 0), a, 0, x, pv, inf) == -8
@@ -265,3 +265,51 @@ def test_options_validation_before_launch(lib):
     assert f(None, a, lu, pv, pv) == -9
     for code in (-11,):
         assert "unknown" not in tdls.strerror(code)
+
+
+def test_interleaved_spans_and_ex_numbering(lib):
+    """Under interleave W the buffers span whole blocks of W systems, so a
+    buffer that starts right after batch systems overlaps; the *_ex calls
+    number their pointer arguments after the options argument."""
+    n, nrhs, batch, W = 8, 1, 10, 4                 # 3 blocks: 12 systems spanned
+    es = 8
+    Opt = tdls.Options
+    a = 1 << 40
+    tight = a + batch * n * n * es                   # fine for W = 1, overlaps for W = 4
+    roomy = a + 12 * n * n * es
+    x = roomy + 12 * n * n * es
+    pv = x + 12 * n * nrhs * es
+    inf = pv + 12 * n * 4
+    f = lambda opt, lu: tdls.tdls_getrf_batched_ex(tdls.F64, tdls.ROW_MAJOR, n, batch, opt, a,
+                                                   lu, pv, inf, 0)
+    assert f(Opt(0, 0, W), tight) == -7
+    assert f(Opt(0, 0, 0), 0) == -7
+    # getrs_ex: [6] opt (no flags), [7] LU, [8] piv, [9] B, [10] X
+    r = lambda opt, *p: tdls.tdls_getrs_batched_ex(tdls.F64, tdls.COL_MAJOR, n, nrhs, batch, opt,
+                                                   *p, 0)
+    assert r(Opt(1, 0, W), a, pv, x, roomy) == -6        # scaling is not a getrs option
+    assert r(Opt(0, 0, batch + 1), a, pv, x, roomy) == -6
+    assert r(Opt(0, 0, W), 0, pv, x, roomy) == -7
+    assert r(Opt(0, 0, W), a, 0, x, roomy) == -8
+    assert r(Opt(0, 0, W), a, pv, 0, roomy) == -9
+    assert r(Opt(0, 0, W), a, pv, x, tight) == -10       # X overlaps LU's span
+    # potrf_ex: [5] shift, [6] opt, [7] A, [8] L, [9] info
+    c = lambda shift, opt, *p: tdls.tdls_potrf_batched_ex(tdls.F64, tdls.ROW_MAJOR, n, batch,
+                                                          shift, opt, *p, 0)
+    assert tdls.tdls_potrf_batched_ex(0, 0, n, -1, 0.0, None, a, roomy, inf, 0) == -4
+    assert c(float("inf"), None, a, roomy, inf) == -5
+    assert c(0.0, Opt(1, 0, 1), a, roomy, inf) == -6
+    assert c(0.0, Opt(0, 0, W), 0, roomy, inf) == -7
+    assert c(0.0, Opt(0, 0, W), a, tight, inf) == -8
+    assert c(0.0, Opt(0, 0, W), a, roomy, 0) == -9
+    # posv_ex: [6] shift, [7] opt, [8] A, [9] B, [10] X, [11] info
+    v = lambda shift, opt, *p: tdls.tdls_posv_batched_ex(tdls.F64, tdls.ROW_MAJOR, n, nrhs, batch,
+                                                         shift, opt, *p, 0)
+    assert v(float("nan"), None, a, roomy, x, inf) == -6
+    assert v(0.0, Opt(0, 3, 1), a, roomy, x, inf) == -7
+    assert v(0.0, Opt(0, 0, W), 0, roomy, x, inf) == -8
+    assert v(0.0, Opt(0, 0, W), a, 0, x, inf) == -9
+    assert v(0.0, Opt(0, 0, W), a, roomy, a, inf) == -10
+    assert v(0.0, Opt(0, 0, W), a, roomy, x, 0) == -11
+    # an empty batch launches nothing, whatever the interleave
+    assert tdls.tdls_posv_batched_ex(1, 0, n, 1, 0, 0.0, Opt(0, 0, 9), 0, 0, 0, 0, 0) == 0
