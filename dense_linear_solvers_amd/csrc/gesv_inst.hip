@@ -43,7 +43,8 @@ template <typename Real, int N, int NRHS, int T>
 static int launch_getrs(const LaunchPlan& p, const void* LU, const void* B, void* X,
                         const int32_t* piv, hipStream_t stream) {
   using S = GetrsShape<Real, N, NRHS, T>;
-  static_assert(S::BLOCK_BYTES == getrs_lds_bytes(N, T), "host and device LDS sizes disagree");
+  static_assert(S::BLOCK_BYTES == getrs_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
+                "host and device LDS sizes disagree");
   if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((getrs_kernel<Real, N, NRHS, T>), dim3((unsigned)p.grid),
                      dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,

@@ -279,9 +279,9 @@ __device__ __forceinline__ uint32_t lo_word(double v) {
 template <int N>
 __device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2; }
 
-// U x = y for the group's system, then X stored (all +0.0 when `failed` or
-// when an entry of x is not finite).  Returns true on the group's lanes
-// when an entry of x (positions below n) is not finite.
+// U x = y for the group's system, then X stored (all +0.0 when `failed` or,
+// with ZERO_NONFINITE, when an entry of x is not finite).  Returns true on
+// the group's lanes when an entry of x (positions below n) is not finite.
 // `ut` is the group's LDS area (at least max(N * NRHS, N (N + 1) / 2)
 // entries).  write_rhs(ut) must store the right-hand sides by position
 // (entry (q, j) at ut[q * NRHS + j]); write_u(ut) must then store row q of U
@@ -297,7 +297,8 @@ __device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2;
 // j = j0 + NJ*jj of the positions ph + P*m, so x_k costs one division per
 // column class on the lanes of phase k % P, handed to the lanes of the same
 // class by a lane fetch; U(q, k) is read from the store.
-template <typename Real, int N, int NRHS, int T, typename WR, typename WU>
+template <typename Real, int N, int NRHS, int T, bool ZERO_NONFINITE = true, typename WR,
+          typename WU>
 __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, bool live,
                                                   bool failed, int64_t sys, int n, int nrhs,
                                                   int col, int64_t ilv, Real* X, WR&& write_rhs,
@@ -382,7 +383,7 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
     });
     xbad = group_any<T>(bad, gbase);
     if (live) {
-      const bool zero = failed || xbad;
+      const bool zero = failed || (ZERO_NONFINITE && xbad);
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
@@ -437,7 +438,7 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
     });
     xbad = group_any<T>(bad, gbase);
     if (live) {
-      const bool zero = failed || xbad;
+      const bool zero = failed || (ZERO_NONFINITE && xbad);
       sfor<0, QR>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         const int q = ph + P * m;

@@ -95,7 +95,7 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   p->shift = 0.0;
   p->flags = 0;
   p->interleave = 1;
-  p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, T)
+  p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, NRHS, T, is64)
                  : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, NRHS, T, is64)
                                                      : gesv_lds_bytes(N, NRHS, T, is64);
   return 0;

@@ -110,9 +110,19 @@ constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
   return kWavesPerBlock * (kWaveSize / T) * group * es;
 }
 
-// LDS bytes of one block (one wave) of the getrs kernel: the swap sequence
-// of each group.
-constexpr int getrs_lds_bytes(int N, int T) { return kWavesPerBlock * (kWaveSize / T) * N * 4; }
+// LDS bytes of one block (one wave) of the getrs kernel: per group, the
+// swap sequence (N int32, rounded up to 16 bytes) and, with four or more
+// right-hand sides, the larger of the right-hand sides by position and a
+// packed triangle (L for the forward, then U for the back substitution).
+constexpr int getrs_lds_bytes(int N, int NRHS, int T, bool is64) {
+  const int es = is64 ? 8 : 4;
+  const int vec = 16 / es;
+  const int piv = (N * 4 + 15) / 16 * 16;
+  const int utri = (N * (N + 1) / 2 + vec - 1) / vec * vec;
+  const int tri = utri > N * NRHS ? utri : N * NRHS;
+  const int elems = NRHS >= 4 ? (tri + vec - 1) / vec * vec : 0;
+  return kWavesPerBlock * (kWaveSize / T) * (piv + elems * es);
+}
 
 // LDS bytes of one block (one wave) of the Cholesky kernel: per group, the
 // largest of a symmetry-check chunk (min(T, 16) rows of stride N + 1), the

@@ -163,7 +163,13 @@ def test_plan_op_validation_and_shapes(lib):
             assert f["group_size"] == g["group_size"] and f["lds_bytes"] == g["lds_bytes"]
             for nrhs in (1, 3, 8):
                 s = tdls.plan_op("getrs", dtype, "col", n, nrhs, 1000)
-                assert s["lds_bytes"] == s["systems_per_wave"] * s["n_kernel"] * 4
+                N, R = s["n_kernel"], s["nrhs_kernel"]
+                es = 8 if dtype == "f64" else 4
+                vec = 16 // es
+                tri = max(-(-(N * (N + 1) // 2) // vec) * vec, N * R)
+                elems = -(-tri // vec) * vec if R >= 4 else 0
+                per_group = -(-(N * 4) // 16) * 16 + elems * es
+                assert s["lds_bytes"] == s["systems_per_wave"] * per_group
                 assert s["systems_per_block"] * s["grid"] >= 1000
 
 
