@@ -25,9 +25,11 @@
 // gfx950 design.  There is no pivot search: row r stays in lane r % T, slot
 // r / T.  The column of multipliers just formed is itself the broadcast
 // source of the rank-1 update: L(c,j) sits in lane c % T, slot c / T, which
-// is the lane a DPP row_newbcast (T = 16) or quad_perm (T = 4) reads, or a
-// readlane (T = 64) — no exchange through LDS.  Only slots that hold rows
-// at or below column c take the update of column c.  The symmetry check and
+// is the lane a DPP row_newbcast (T = 16) or quad_perm (T = 4) reads, with
+// no exchange through LDS.  A whole-wave group (T = 64) spans four DPP rows,
+// so its column goes through LDS once per step and each row reads back the
+// entries it broadcasts.  Only slots that hold rows at or below column c
+// take the update of column c.  The symmetry check and
 // the back substitution read a row-major copy of the matrix (then of L) in
 // LDS with an odd row stride.
 #pragma once
@@ -276,8 +278,30 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       }
     });
     // rank-1 update of the columns right of j, on the slots holding rows at
-    // or below each column; L(c, j) comes from lane c % T, slot c / T
-    sfor<j + 1, N>([&](auto cc) {
+    // or below each column; L(c, j) comes from lane c % T, slot c / T.  A
+    // whole-wave group stages the column through LDS so that every 16-lane
+    // row holds the entries it serves, then broadcasts by DPP inside the
+    // fused multiply-add (instead of two readlanes per entry).
+    if constexpr (T == 64) {
+      static_assert(R == 1, "one row per lane in whole-wave groups");
+      if (tx > j && tx < N) sq[tx] = a[0][j];
+      wave_sync_lds();
+      constexpr int NU = (N + 15) / 16;
+      constexpr int U0 = (j + 1) / 16;
+      // one 16-entry block at a time keeps one source register live
+      sfor<U0, NU>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const Real uc = sq[r * 16 + (tx & 15)];
+        constexpr int c0 = r * 16 > j + 1 ? r * 16 : j + 1;
+        constexpr int c1 = (r + 1) * 16 < N ? (r + 1) * 16 : N;
+        sfor<c0, c1>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          fnmac_bcast<T, c % 16, c == c0>(a[0][c], uc, lm[0]);
+        });
+      });
+      wave_sync_lds();   // read before the next column is written
+    }
+    if constexpr (T != 64) sfor<j + 1, N>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
       constexpr int cs = c / T;
       constexpr int cl = c % T;
@@ -289,15 +313,6 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           if constexpr (K >= js)
             fnmac_bcast<T, cl % SL, K == cs && (c == j + 1 || cl == 0)>(a[K][c], a[cs][j],
                                                                         lm[K]);
-        });
-      } else {
-        // a few readlanes at a time: hoisted all together they fill the
-        // scalar registers
-        if constexpr (c % 8 == 0) __builtin_amdgcn_sched_barrier(0);
-        const Real lc = group_bcast<T, cl>(a[cs][j]);
-        sfor<cs, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          if constexpr (K >= js) a[K][c] = __builtin_fma(-lm[K], lc, a[K][c]);
         });
       }
     });
