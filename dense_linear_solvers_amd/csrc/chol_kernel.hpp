@@ -115,7 +115,12 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   const bool live = sys < batch;
   Real* sq = reinterpret_cast<Real*>(lds_raw + wave * S::WAVE_BYTES) + g * S::GROUP_ELEMS;
 
-  // ---- load: row q = tx + K*T of A and of B; past n the identity and zero
+  // ---- load: row q = tx + K*T of A and of B; past n the identity and zero.
+  // With several right-hand sides and whole-wave groups B is loaded after
+  // the factorization (it plays no part in it), which keeps its registers
+  // free meanwhile (n = 64 with 8: 171 -> 161 VGPRs, a third wave per SIMD);
+  // smaller groups keep their occupancy either way and load it up front.
+  constexpr bool LATE_B = !FACT && NRHS > 1 && T == 64;
   Real a[R][N];
   Real y[R][NRHS];
   {
@@ -137,7 +142,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           });
           sfor<0, NRHS>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            if constexpr (FACT)
+            if constexpr (FACT || LATE_B)
               y[K][j] = Real(0);
             else
               y[K][j] = br[COL ? j * N : j];
@@ -162,7 +167,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         sfor<0, NRHS>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           y[K][j] = Real(0);
-          if constexpr (!FACT)
+          if constexpr (!FACT && !LATE_B)
             if (qrow && j < nrhs)
               y[K][j] = Bs[(col ? (int64_t)j * n + qq : (int64_t)qq * nrhs + j) * ilv];
         });
@@ -317,6 +322,27 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       }
     });
   });
+
+  if constexpr (LATE_B) {
+    // the right-hand sides, and their part of the input check (-1 outranks
+    // every other status)
+    const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
+    bool bbad = false;
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      const bool qrow = live && q < n;
+      const int qq = qrow ? q : 0;
+      sfor<0, NRHS>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        y[K][j] = Real(0);
+        if (qrow && j < nrhs)
+          y[K][j] = Bs[(col ? (int64_t)j * n + qq : (int64_t)qq * nrhs + j) * ilv];
+        bbad |= not_finite(y[K][j]);
+      });
+    });
+    status = group_any<T>(bbad, g * T) ? -1 : status;
+  }
 
   if constexpr (FACT) {
     // ---- L in the layout of A, zero above the diagonal; zero when failed
