@@ -14,7 +14,7 @@ object prices the kernel's algorithmic HBM bytes per launch against 8 TB/s;
 same inputs.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
-                  [--op gesv|getrf|getrs|potrf|posv] [--no-cpu]
+                  [--op gesv|getrf|getrs|potrf|posv] [--interleave W] [--no-cpu]
   python bench.py --calibrate-copy      # a plain 1 GiB device copy, for
                                         # scaling the HBM byte counters
   python bench.py [--workload NAME] [--op OP] --summarize-counters \
@@ -154,6 +154,22 @@ def summarize_counters(workload: str, op: str, fetch_dir: str, write_dir: str,
     return d
 
 
+def interleave(x: np.ndarray, W: int) -> np.ndarray:
+    """[batch, ...] -> [blocks, ..., W]: element e of system s at
+    (s // W) W E + s % W + e W (the last block padded with zeros)."""
+    batch = x.shape[0]
+    blocks = -(-batch // W)
+    pad = np.zeros((blocks * W,) + x.shape[1:], dtype=x.dtype)
+    pad[:batch] = x
+    pad = pad.reshape((blocks, W) + x.shape[1:])
+    return np.ascontiguousarray(np.moveaxis(pad, 1, -1))
+
+
+def deinterleave(t, batch: int):
+    """Inverse of ``interleave`` for a torch tensor."""
+    return t.movedim(-1, 1).reshape((-1,) + tuple(t.shape[1:-1]))[:batch].contiguous()
+
+
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -225,6 +241,9 @@ def main():
                          "getrs (solve from factors made, untimed, by getrf), or the Cholesky "
                          "potrf / posv (on an spd_* workload)")
     ap.add_argument("--batch", type=int, default=0, help="override the recipe's batch")
+    ap.add_argument("--interleave", type=int, default=1,
+                    help="store the batch with W systems interleaved element by element "
+                         "(W = batch: structure of arrays); the *_ex calls")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
@@ -259,29 +278,34 @@ def main():
           f"{w.layout} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
     dev = torch.device("cuda:0")
-    A = torch.from_numpy(w.A).to(dev)
-    B = torch.from_numpy(w.B).to(dev)
+    W = max(1, args.interleave)
+    if W > w.batch:
+        raise SystemExit("--interleave must not exceed the batch")
+    ex = {"interleave": W, "batch": w.batch} if W > 1 else {}
+    A = torch.from_numpy(interleave(w.A, W) if W > 1 else w.A).to(dev)
+    B = torch.from_numpy(interleave(w.B, W) if W > 1 else w.B).to(dev)
     X = torch.empty_like(B)
-    piv = torch.empty((w.batch, w.n), dtype=torch.int32, device=dev)
+    piv = torch.empty((A.shape[0], w.n, W) if W > 1 else (w.batch, w.n), dtype=torch.int32,
+                      device=dev)
     info = torch.empty((w.batch,), dtype=torch.int32, device=dev)
     out = (X, piv, info)
     stream = torch.cuda.current_stream(dev)
     op = args.op
     plan = tdls.plan_op(op, w.dtype, w.layout, w.n, w.nrhs, w.batch)
     if op == "gesv":
-        step = lambda: tdls.gesv_batched(A, B, w.layout, out=out)
+        step = lambda: tdls.gesv_batched(A, B, w.layout, out=out, **ex)
     elif op == "getrf":
         LU = torch.empty_like(A)
-        step = lambda: tdls.getrf_batched(A, w.layout, out=(LU, piv, info))
+        step = lambda: tdls.getrf_batched(A, w.layout, out=(LU, piv, info), **ex)
     elif op == "getrs":
         LU = torch.empty_like(A)
-        tdls.getrf_batched(A, w.layout, out=(LU, piv, info))     # factors, untimed
-        step = lambda: tdls.getrs_batched(LU, piv, B, w.layout, out=X)
+        tdls.getrf_batched(A, w.layout, out=(LU, piv, info), **ex)     # factors, untimed
+        step = lambda: tdls.getrs_batched(LU, piv, B, w.layout, out=X, **ex)
     elif op == "potrf":
         Lc = torch.empty_like(A)
-        step = lambda: tdls.potrf_batched(A, w.layout, out=(Lc, info))
+        step = lambda: tdls.potrf_batched(A, w.layout, out=(Lc, info), **ex)
     else:
-        step = lambda: tdls.posv_batched(A, B, w.layout, out=(X, info))
+        step = lambda: tdls.posv_batched(A, B, w.layout, out=(X, info), **ex)
 
     for _ in range(args.warmup):
         step()
@@ -303,11 +327,13 @@ def main():
     # sanity of the timed output (no oracle here): status and a residual
     # sample (for getrf: the solve of the timed factors)
     if op == "getrf":
-        tdls.getrs_batched(LU, piv, B, w.layout, out=X)
+        tdls.getrs_batched(LU, piv, B, w.layout, out=X, **ex)
         torch.cuda.synchronize()
     if op == "potrf":
-        tdls.posv_batched(A, B, w.layout, out=(X, info))
+        tdls.posv_batched(A, B, w.layout, out=(X, info), **ex)
         torch.cuda.synchronize()
+    if W > 1:   # back to one system after another for the check
+        A, B, X = (deinterleave(t, w.batch) for t in (A, B, X))
     info_h = info.cpu().numpy()
     rng = np.random.default_rng(0)
     sample = torch.from_numpy(rng.choice(w.batch, size=min(w.batch, 512), replace=False)).to(dev)
@@ -344,6 +370,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "op": op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
+                   **({"interleave": W} if W > 1 else {}),
                    "layout": "column-major" if w.layout == "col" else "row-major",
                    "distribution": w.meta.get("recipe"), "seed": 0,
                    **({"gap_filtered": False} if "gap_filtered" in w.meta else {}),
