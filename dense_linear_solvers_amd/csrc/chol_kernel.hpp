@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   const int wave = threadIdx.x / kWaveSize;
   const int g = lane / T;
   const int tx = lane & (T - 1);
-  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * G;
+  const int64_t wave_first = (block_of(ilv) * kWavesPerBlock + wave) * G;
   if (wave_first >= batch) return;  // the whole wave is past the batch
   const int64_t sys = wave_first + g;
   const bool live = sys < batch;

@@ -254,6 +254,23 @@ __device__ __forceinline__ bool group_any(bool v, int gbase) {
 __device__ __forceinline__ bool not_finite(double v) { return !__builtin_isfinite(v); }
 __device__ __forceinline__ bool not_finite(float v) { return !__builtin_isfinite(v); }
 
+// Block of systems a workgroup takes.  Workgroups go to the 8 XCDs of the
+// chip in turn (workgroup b on XCD b mod 8), each XCD with its own L2.  One
+// after another (interleave 1) a block's systems fill whole cache lines by
+// themselves, and blocks follow the workgroup order.  Interleaved, a cache
+// line holds the same element of neighbouring blocks, so the blocks are
+// renumbered to give each XCD a contiguous range: its L2 then serves the
+// neighbours from one fetch instead of each XCD fetching the line.
+__device__ __forceinline__ int64_t block_of(int64_t ilv) {
+  const int64_t b = blockIdx.x;
+  if (ilv == 1) return b;
+  constexpr int64_t kXcds = 8;
+  const int64_t nb = gridDim.x;
+  const int64_t q = nb / kXcds, r = nb % kXcds;
+  const int64_t x = b % kXcds, i = b / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
 // Start of system s in a batch of systems of E elements each, stored with W
 // systems interleaved element by element (the single strided form of the
 // TDLS page, section Residency: W = 1 one system after another, W = batch
@@ -482,7 +499,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   const int g = lane / T;
   const int tx = lane & (T - 1);
   const int gbase = g * T;  // first lane of the group
-  const int64_t wave_first = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * G;
+  const int64_t wave_first = (block_of(ilv) * kWavesPerBlock + wave) * G;
   if (wave_first >= batch) return;  // the whole wave is past the batch
   const int64_t sys = wave_first + g;
   const bool live = sys < batch;
