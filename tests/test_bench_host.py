@@ -1,0 +1,64 @@
+"""bench.py's host-side pieces (CPU only): the algorithmic work per system
+against hand counts, the interleaving of its inputs against the element
+formula of the C interface, the source hash that keys the committed HBM
+counters, and the one-GPU guard."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_algorithmic_bytes_and_flops_by_hand():
+    # n = 2, nrhs = 1, float64.  gesv: A 32 B, B and X 16 B each, piv 8, info 4
+    assert bench.algorithmic_bytes(2, 1, 8, "gesv") == 32 + 32 + 8 + 4
+    assert bench.algorithmic_bytes(2, 1, 8, "getrf") == 64 + 8 + 4
+    assert bench.algorithmic_bytes(2, 1, 8, "getrs") == 32 + 8 + 32
+    assert bench.algorithmic_bytes(2, 1, 8, "potrf") == 64 + 4
+    assert bench.algorithmic_bytes(2, 1, 8, "posv") == 32 + 32 + 4
+    # elimination of a 2 x 2: one division and one multiply-add (2 flops);
+    # substitution: forward 1 multiply-add, back 2 divisions + 1 multiply-add
+    assert bench.algorithmic_flops(2, 1, "getrf") == 3
+    assert bench.algorithmic_flops(2, 1, "getrs") == 2 * 2 * 1 + 2
+    assert bench.algorithmic_flops(2, 1, "gesv") == 3 + 6
+    # Cholesky 2 x 2: sqrt, division, multiply-add, sqrt = 1 + 1 + 2 + 1
+    assert bench.algorithmic_flops(2, 1, "potrf") == 5
+    # the headline: 8,836 B and 23,344 flops per system
+    assert bench.algorithmic_bytes(32, 1, 8, "gesv") == 8836
+    assert bench.algorithmic_flops(32, 1, "gesv") == 23344
+
+
+@pytest.mark.parametrize("W", [2, 3, 7])
+def test_interleave_matches_the_element_formula(W):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(W)
+    x = rng.standard_normal((10, 3, 4))
+    y = bench.interleave(x, W)
+    flat = y.reshape(-1)
+    E = 12
+    for s in range(10):
+        for e in range(E):
+            assert flat[(s // W) * W * E + s % W + e * W] == x[s].reshape(-1)[e]
+    back = bench.deinterleave(torch.from_numpy(y), 10).numpy()
+    np.testing.assert_array_equal(back, x)
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) {\n  // a comment\n  return x + 1; /* another */\n}\n"
+    b = "int f(int x) {\n\n  return x + 1;\n}\n"
+    c = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
