@@ -72,10 +72,10 @@ def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
 
 
 def _code_only(text: str) -> str:
-    """C/C++ source without comments and blank lines (so that a comment edit
-    does not mark the counters as stale)."""
+    """C/C++ source without comments, blank lines and indentation (so that a
+    comment or layout edit does not mark the counters as stale)."""
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    lines = (" ".join(re.sub(r"//.*$", "", ln).split()) for ln in text.splitlines())
     return "\n".join(ln for ln in lines if ln)
 
 

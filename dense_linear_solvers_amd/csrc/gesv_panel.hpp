@@ -987,53 +987,52 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       if (tx == 0) info[sys] = status;
     }
   } else {
+    // ---- back substitution (see upper_solve_store): every row, whatever lane
+    // holds it, stores its right-hand sides and then its U entries (columns
+    // from its position on) by position
+    int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
+    wave_sync_lds();  // the last records have been read
+    const bool xbad = upper_solve_store<Real, N, NRHS, T>(
+        rec, tx, gbase, live, status != 0 || nf != 0, live ? sys : 0, n, nrhs, col, ilv, X,
+        [&](Real* yt) {
+          sfor<0, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            const int q = lab[K];
+            if (q >= 0) {
+              sfor<0, NRHS>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                yt[q * NRHS + j] = y[K][j];
+              });
+            }
+          });
+        },
+        [&](Real* ut) {
+          sfor<0, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            const int q = lab[K];
+            if (q >= 0) {
+              Real* row = ut + utri_row<N>(q) - q;   // entry of column c at row[c]
+              sfor<0, N>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                if (c >= q) row[c] = a[K][c];
+              });
+            }
+          });
+        });
 
-  // ---- back substitution (see upper_solve_store): every row, whatever lane
-  // holds it, stores its right-hand sides and then its U entries (columns
-  // from its position on) by position
-  int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
-  wave_sync_lds();  // the last records have been read
-  const bool xbad = upper_solve_store<Real, N, NRHS, T>(
-      rec, tx, gbase, live, status != 0 || nf != 0, live ? sys : 0, n, nrhs, col, ilv, X,
-      [&](Real* yt) {
-        sfor<0, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          const int q = lab[K];
-          if (q >= 0) {
-            sfor<0, NRHS>([&](auto jc) {
-              constexpr int j = decltype(jc)::value;
-              yt[q * NRHS + j] = y[K][j];
-            });
-          }
-        });
-      },
-      [&](Real* ut) {
-        sfor<0, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          const int q = lab[K];
-          if (q >= 0) {
-            Real* row = ut + utri_row<N>(q) - q;   // entry of column c at row[c]
-            sfor<0, N>([&](auto cc) {
-              constexpr int c = decltype(cc)::value;
-              if (c >= q) row[c] = a[K][c];
-            });
-          }
-        });
+    if (status == 0 && (nf != 0 || xbad)) status = -3;
+    const bool failed = status != 0;
+
+    // ---- piv (all -1 for a failed system) and info
+    if (live) {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        if (q < n) Ps[q * ilv] = failed ? -1 : pv[K];
       });
-
-  if (status == 0 && (nf != 0 || xbad)) status = -3;
-  const bool failed = status != 0;
-
-  // ---- piv (all -1 for a failed system) and info
-  if (live) {
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      if (q < n) Ps[q * ilv] = failed ? -1 : pv[K];
-    });
-    if (tx == 0) info[sys] = status;
+      if (tx == 0) info[sys] = status;
+    }
   }
-  }  // gesv
 }
 
 }  // namespace tdls
