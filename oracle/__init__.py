@@ -27,7 +27,7 @@ import numpy as np
 
 from .build import build, library_path
 
-__all__ = ["gesv", "getrf", "getrs", "potrf", "posv", "pivot_gap", "build", "library_path", "to_storage", "from_storage",
+__all__ = ["gesv", "getrf", "getrs", "potrf", "potrs", "posv", "pivot_gap", "build", "library_path", "to_storage", "from_storage",
            "rhs_to_storage", "rhs_from_storage", "max_threads", "use_library"]
 
 _LAYOUTS = {"row": 0, "col": 1}
@@ -57,6 +57,10 @@ def _load():
             c.restype = ctypes.c_int
             c.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_double, tp, tp,
                           i32p, ctypes.c_int]
+            t = getattr(lib, "oracle_potrs_" + sfx)
+            t.restype = ctypes.c_int
+            t.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, tp, tp, tp,
+                          ctypes.c_int]
             v = getattr(lib, "oracle_posv_" + sfx)
             v.restype = ctypes.c_int
             v.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
@@ -247,6 +251,28 @@ def potrf(A_store: np.ndarray, n: int, layout: str = "row", shift: float = 0.0,
     if rc != 0:
         raise RuntimeError(f"oracle_potrf_{sfx} returned {rc}")
     return L, info
+
+
+def potrs(L_store: np.ndarray, B_store: np.ndarray, n: int, nrhs: int, layout: str = "row",
+          nthreads: int = 0) -> np.ndarray:
+    """Solve from Cholesky factors: ``L_store`` is the storage (in
+    ``layout``) of L as potrf writes it (lower triangle read; a system whose
+    L(0,0) is 0, a failed factorization, gets X = +0.0).  Returns X in B's
+    storage."""
+    sfx, ct = _sfx(L_store.dtype)
+    if np.dtype(B_store.dtype) != np.dtype(L_store.dtype):
+        raise TypeError("L and B must share a dtype")
+    L = np.ascontiguousarray(L_store).reshape(-1)
+    B = np.ascontiguousarray(B_store).reshape(-1)
+    batch = L.size // (n * n)
+    if L.size != batch * n * n or B.size != batch * n * nrhs:
+        raise ValueError("L and B sizes do not agree")
+    X = np.empty_like(B)
+    rc = getattr(_load(), "oracle_potrs_" + sfx)(
+        _LAYOUTS[layout], n, nrhs, batch, _ptr(L, ct), _ptr(B, ct), _ptr(X, ct), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_potrs_{sfx} returned {rc}")
+    return X.reshape(np.shape(B_store))
 
 
 def posv(A_store: np.ndarray, B_store: np.ndarray, n: int, nrhs: int, layout: str = "row",

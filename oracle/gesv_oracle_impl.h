@@ -496,6 +496,79 @@ int SFX(oracle_potrf)(int layout, int n, int64_t batch, double shift, const REAL
     return 0;
 }
 
+/*
+ * potrs of one system: X from the Cholesky factor that potrf writes (L on
+ * and below the diagonal, in the layout of A; the entries above it are not
+ * read), by L y = b and L^T x = y in exactly the order of posv_one, so
+ * potrf then potrs gives posv's solution.  A failed factorization leaves L
+ * all +0.0 (ruSOLVER contract), so L(0,0) == 0 marks it, and x = +0.0.
+ * There is no status: a zero or non-finite factor entry flows into x.
+ */
+static void SFX(potrs_one)(int layout, int n, int nrhs, const REAL *l, const REAL *b, REAL *x,
+                           REAL *Y)
+{
+    if (SFX(load_a)(l, layout, n, 0, 0) == 0) {
+        SFX(zero_rhs)(layout, n, nrhs, x);
+        return;
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)r * nrhs + j] = b[SFX(rhs_index)(layout, n, nrhs, r, j)];
+    /* L y = b: y_k = y_k / L(k,k), then y_k leaves the rows below */
+    for (int k = 0; k < n; ++k) {
+        const REAL d = SFX(load_a)(l, layout, n, k, k);
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / d;
+        for (int i = k + 1; i < n; ++i) {
+            const REAL lik = SFX(load_a)(l, layout, n, i, k);
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)i * nrhs + j] = FMA(-lik, Y[(size_t)k * nrhs + j], Y[(size_t)i * nrhs + j]);
+        }
+    }
+    /* L^T x = y: x_k = y_k / L(k,k), then x_k leaves the rows above with L(k,i) */
+    for (int k = n - 1; k >= 0; --k) {
+        const REAL d = SFX(load_a)(l, layout, n, k, k);
+        for (int j = 0; j < nrhs; ++j)
+            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / d;
+        for (int i = 0; i < k; ++i) {
+            const REAL lki = SFX(load_a)(l, layout, n, k, i);
+            for (int j = 0; j < nrhs; ++j)
+                Y[(size_t)i * nrhs + j] = FMA(-lki, Y[(size_t)k * nrhs + j], Y[(size_t)i * nrhs + j]);
+        }
+    }
+    for (int r = 0; r < n; ++r)
+        for (int j = 0; j < nrhs; ++j)
+            x[SFX(rhs_index)(layout, n, nrhs, r, j)] = Y[(size_t)r * nrhs + j];
+}
+
+int SFX(oracle_potrs)(int layout, int n, int nrhs, int64_t batch, const REAL *L, const REAL *B,
+                      REAL *X, int nthreads)
+{
+    int rc = oracle_check_args(layout, n, nrhs, batch);
+    if (rc != 0)
+        return rc;
+    if (batch == 0)
+        return 0;
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        REAL *Y = (REAL *)malloc(sizeof(REAL) * (size_t)n * nrhs);
+        if (Y == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t s = 0; s < batch; ++s)
+                SFX(potrs_one)(layout, n, nrhs, L + s * (int64_t)n * n, B + s * (int64_t)n * nrhs,
+                               X + s * (int64_t)n * nrhs, Y);
+        }
+        free(Y);
+    }
+    return failed ? ORACLE_ENOMEM : 0;
+}
+
 int SFX(oracle_posv)(int layout, int n, int nrhs, int64_t batch, double shift, const REAL *A,
                      const REAL *B, REAL *X, int32_t *info, int nthreads)
 {

@@ -85,6 +85,15 @@ MUTANTS = {
                                   "    return 0;"),
     "posv_solution_check_dropped": ("        SFX(zero_rhs)(layout, n, nrhs, x); /* x */\n        return -3;",
                                     "        (void)0;"),
+    "potrs_back_transposed": ("const REAL lki = SFX(load_a)(l, layout, n, k, i);",
+                              "const REAL lki = SFX(load_a)(l, layout, n, i, k);"),
+    "potrs_forward_no_division": (
+        "        const REAL d = SFX(load_a)(l, layout, n, k, k);\n        for (int j = 0; j < nrhs; ++j)\n"
+        "            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] / d;\n        for (int i = k + 1;",
+        "        const REAL d = SFX(load_a)(l, layout, n, k, k);\n        for (int j = 0; j < nrhs; ++j)\n"
+        "            Y[(size_t)k * nrhs + j] = Y[(size_t)k * nrhs + j] + 0 * d;\n        for (int i = k + 1;"),
+    "potrs_failed_not_detected": ("    if (SFX(load_a)(l, layout, n, 0, 0) == 0) {",
+                                  "    if (0) {"),
     "getrs_failed_negative_zero": (
         "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = (REAL)0;\n        return;",
         "x[SFX(rhs_index)(layout, n, nrhs, r, j)] = -(REAL)0;\n        return;"),
@@ -114,6 +123,8 @@ def _selection():
     yield lambda: pins.test_scaling_by_power_of_two_is_exact(np.float64, "row")
     yield lambda: pins.test_scaling_general(np.float64)
     yield lambda: pins.test_cholesky_nonfinite_statuses(np.float32)
+    yield lambda: pins.test_potrs_exact_integer_factors(np.float64, "col")
+    yield lambda: pins.test_potrs_matches_lapack_and_posv(np.float64)
 
 
 def _build_variant(tmp_path, name, mutation):

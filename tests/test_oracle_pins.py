@@ -800,3 +800,48 @@ def test_cholesky_nonfinite_statuses(dtype):
     # a non-positive pivot comes before -3
     Aneg = np.array([[[-1, 0], [0, 1]]], dtype)
     assert oracle.potrf(Aneg, 2, "row")[1][0] == 1
+
+
+# ----------------------------------------------------------------- potrs
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_potrs_exact_integer_factors(dtype, layout):
+    """An integer L with a diagonal of powers of two and b = L L^T x for an
+    integer x: both substitutions meet exact quotients only, so x comes out
+    exactly; the entries above the diagonal are not read."""
+    rng = np.random.default_rng(51)
+    for n, nrhs in [(1, 1), (3, 2), (7, 1), (10, 4)]:
+        L, A, x, b = _exact_spd(rng, n, nrhs)
+        Lg = L.astype(dtype) + np.triu(rng.integers(5, 9, (n, n)), 1).astype(dtype)
+        X = oracle.potrs(oracle.to_storage(Lg[None], layout),
+                         oracle.rhs_to_storage(b[None].astype(dtype), layout), n, nrhs, layout)
+        np.testing.assert_array_equal(oracle.rhs_from_storage(X, layout, n, nrhs)[0],
+                                      x.astype(dtype), err_msg=f"n={n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_potrs_matches_lapack_and_posv(dtype):
+    """Against LAPACK's potrs (scipy cho_solve on the same factor) within the
+    working-precision bound; potrf then potrs is posv bit for bit (the same
+    operations in the same order); a failed factorization (L all +0.0)
+    gives X = +0.0."""
+    rng = np.random.default_rng(52)
+    n, nrhs, batch = 9, 3, 20
+    G = rng.standard_normal((batch, n, n))
+    A = (G @ G.transpose(0, 2, 1) / n + np.eye(n)).astype(dtype)
+    A = np.tril(A) + np.tril(A, -1).transpose(0, 2, 1)
+    B = rng.standard_normal((batch, n, nrhs)).astype(dtype)
+    L, info = oracle.potrf(A, n, "row")
+    assert (info == 0).all()
+    X = oracle.potrs(L, B, n, nrhs, "row")
+    Xp, _ = oracle.posv(A, B, n, nrhs, "row")
+    np.testing.assert_array_equal(X, Xp)
+    u = float(np.finfo(dtype).eps)
+    for s in range(batch):
+        ref = scipy.linalg.cho_solve((L[s].astype(np.float64), True), B[s].astype(np.float64))
+        kappa = np.linalg.cond(A[s].astype(np.float64), np.inf)
+        assert np.abs(X[s] - ref).max() / np.abs(ref).max() <= 20 * n * kappa * u
+    Xz = oracle.potrs(np.zeros((2, n, n), dtype), B[:2], n, nrhs, "row")
+    assert (Xz == 0).all() and not np.signbit(Xz).any()
