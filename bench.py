@@ -14,7 +14,7 @@ object prices the kernel's algorithmic HBM bytes per launch against 8 TB/s;
 same inputs.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
-                  [--op gesv|getrf|getrs|potrf|posv] [--interleave W] [--no-cpu]
+                  [--op gesv|getrf|getrs|potrf|potrs|posv] [--interleave W] [--no-cpu]
   python bench.py --calibrate-copy      # a plain 1 GiB device copy, for
                                         # scaling the HBM byte counters
   python bench.py [--workload NAME] [--op OP] --summarize-counters \
@@ -50,6 +50,8 @@ def algorithmic_bytes(n: int, nrhs: int, es: int, op: str = "gesv") -> int:
         return n * n * es + 4 * n + 2 * n * nrhs * es
     if op == "potrf":                    # A read, L written, info
         return 2 * n * n * es + 4
+    if op == "potrs":                    # L, B read, X written
+        return n * n * es + 2 * n * nrhs * es
     if op == "posv":                     # A, B read, X, info written
         return n * n * es + 2 * n * nrhs * es + 4
     return n * n * es + 2 * n * nrhs * es + 4 * n + 4
@@ -59,7 +61,8 @@ def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
     """Per system: elimination 2*sum(m^2) multiply-add flops plus sum(m)
     divisions (m = n-1 .. 1), forward and back substitution on nrhs columns
     2*n*(n-1) + n each; getrf counts the elimination, getrs the
-    substitutions."""
+    substitutions.  Cholesky: the factorization below, and solves that
+    divide in both substitutions (2*n*(n-1) + 2*n per column)."""
     s2 = sum(m * m for m in range(1, n))
     s1 = sum(range(1, n))
     elim = 2 * s2 + s1
@@ -67,8 +70,10 @@ def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
     # Cholesky: column j costs j multiply-adds for the diagonal, (n-1-j)*j
     # for the entries below it, one square root and n-1-j divisions
     chol = sum(2 * j + 1 + (n - 1 - j) * (2 * j + 1) for j in range(n))
-    return {"getrf": elim, "getrs": subst, "potrf": chol,
-            "posv": chol + subst}.get(op, elim + subst)
+    # Cholesky solves divide in both substitutions
+    chol_subst = nrhs * (2 * n * (n - 1) + 2 * n)
+    return {"getrf": elim, "getrs": subst, "potrf": chol, "potrs": chol_subst,
+            "posv": chol + chol_subst}.get(op, elim + subst)
 
 
 def _code_only(text: str) -> str:
@@ -91,7 +96,8 @@ def kernel_source_hash() -> str:
 
 # the kernel each op launches (rocprofv3 -T truncates names to these)
 KERNEL_OF_OP = {"gesv": "gesv_panel_kernel", "getrf": "gesv_panel_kernel",
-                "getrs": "getrs_kernel", "potrf": "chol_kernel", "posv": "chol_kernel"}
+                "getrs": "getrs_kernel", "potrf": "chol_kernel", "potrs": "chol_kernel",
+                "posv": "chol_kernel"}
 
 
 def traffic_path(workload: str, op: str) -> str:
@@ -195,6 +201,9 @@ def cpu_baseline(w, op: str = "gesv", min_seconds: float = 10.0,
     A = np.ascontiguousarray(w.A)
     B = np.ascontiguousarray(w.B)
     n, nrhs, layout = w.n, w.nrhs, w.layout
+    if op == "potrs":
+        Lf, _ = oracle.potrf(A, n, layout, nthreads=cores)
+        Lf = oracle.to_storage(Lf, layout)
     if op == "getrs":
         LU, ipiv, finfo, _ = oracle.getrf(A, n, layout, nthreads=cores)
         LU = oracle.to_storage(LU, layout)
@@ -207,6 +216,8 @@ def cpu_baseline(w, op: str = "gesv", min_seconds: float = 10.0,
             oracle.potrf(A[:cnt], n, layout, nthreads=cores)
         elif op == "posv":
             oracle.posv(A[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
+        elif op == "potrs":
+            oracle.potrs(Lf[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
         elif op == "getrs":
             oracle.getrs(LU[:cnt], ipiv[:cnt], B[:cnt], n, nrhs, layout, nthreads=cores)
         else:
@@ -236,10 +247,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--op", default="gesv", choices=["gesv", "getrf", "getrs", "potrf", "posv"],
+    ap.add_argument("--op", default="gesv",
+                    choices=["gesv", "getrf", "getrs", "potrf", "potrs", "posv"],
                     help="gesv (default: factor and solve in one call), getrf (factor only), "
                          "getrs (solve from factors made, untimed, by getrf), or the Cholesky "
-                         "potrf / posv (on an spd_* workload)")
+                         "potrf / potrs (from factors made, untimed, by potrf) / posv (on an "
+                         "spd_* workload)")
     ap.add_argument("--batch", type=int, default=0, help="override the recipe's batch")
     ap.add_argument("--interleave", type=int, default=1,
                     help="store the batch with W systems interleaved element by element "
@@ -304,6 +317,10 @@ def main():
     elif op == "potrf":
         Lc = torch.empty_like(A)
         step = lambda: tdls.potrf_batched(A, w.layout, out=(Lc, info), **ex)
+    elif op == "potrs":
+        Lc = torch.empty_like(A)
+        tdls.potrf_batched(A, w.layout, out=(Lc, info), **ex)     # factors, untimed
+        step = lambda: tdls.potrs_batched(Lc, B, w.layout, out=X, **ex)
     else:
         step = lambda: tdls.posv_batched(A, B, w.layout, out=(X, info), **ex)
 

@@ -49,10 +49,11 @@ SCALE_MAXABS = 1
 EXPORTED = ("tdls_gesv_batched", "tdls_gesv_batched_ex", "tdls_getrf_batched",
             "tdls_getrf_batched_ex", "tdls_getrs_batched", "tdls_getrs_batched_ex",
             "tdls_plan_gesv", "tdls_plan_op", "tdls_posv_batched", "tdls_posv_batched_ex",
-            "tdls_potrf_batched", "tdls_potrf_batched_ex", "tdls_strerror", "tdls_version")
-OP_GESV, OP_GETRF, OP_GETRS, OP_POTRF, OP_POSV = 0, 1, 2, 3, 4
+            "tdls_potrf_batched", "tdls_potrf_batched_ex", "tdls_potrs_batched",
+            "tdls_potrs_batched_ex", "tdls_strerror", "tdls_version")
+OP_GESV, OP_GETRF, OP_GETRS, OP_POTRF, OP_POSV, OP_POTRS = 0, 1, 2, 3, 4, 5
 _OPS = {"gesv": OP_GESV, "getrf": OP_GETRF, "getrs": OP_GETRS, "potrf": OP_POTRF,
-        "posv": OP_POSV}
+        "posv": OP_POSV, "potrs": OP_POTRS}
 
 
 def library_path() -> str:
@@ -99,6 +100,15 @@ def load_library():
                                          ctypes.POINTER(Options), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]
+    lib.tdls_potrs_batched.restype = ctypes.c_int
+    lib.tdls_potrs_batched.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.tdls_potrs_batched_ex.restype = ctypes.c_int
+    lib.tdls_potrs_batched_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.POINTER(Options),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
     lib.tdls_plan_gesv.restype = ctypes.c_int
     lib.tdls_plan_gesv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int64, ctypes.POINTER(Plan)]
@@ -185,6 +195,20 @@ def tdls_posv_batched_ex(dtype: int, layout: int, n: int, nrhs: int, batch: int,
     return int(load_library().tdls_posv_batched_ex(int(dtype), int(layout), int(n), int(nrhs),
                                                    int(batch), float(shift), _opt(opt), A, B, X,
                                                    info, stream))
+
+
+def tdls_potrs_batched(dtype: int, layout: int, n: int, nrhs: int, batch: int, L: int, B: int,
+                       X: int, stream: int) -> int:
+    """The C call itself, raw pointers (ints) in, return code out."""
+    return int(load_library().tdls_potrs_batched(int(dtype), int(layout), int(n), int(nrhs),
+                                                 int(batch), L, B, X, stream))
+
+
+def tdls_potrs_batched_ex(dtype: int, layout: int, n: int, nrhs: int, batch: int, opt, L: int,
+                          B: int, X: int, stream: int) -> int:
+    """The C call with options (an Options or None), raw pointers in."""
+    return int(load_library().tdls_potrs_batched_ex(int(dtype), int(layout), int(n), int(nrhs),
+                                                    int(batch), _opt(opt), L, B, X, stream))
 
 
 def tdls_plan_gesv(dtype: int, layout: int, n: int, nrhs: int, batch: int):
@@ -477,6 +501,32 @@ def potrf_batched(A, layout: str = "row", shift: float = 0.0, out=None, stream=N
     if rc != 0:
         raise TdlsError(rc, "tdls_potrf_batched")
     return L, info
+
+
+def potrs_batched(L, B, layout: str = "row", out=None, stream=None, interleave: int = 1,
+                  batch=None):
+    """Solve from Cholesky factors of potrf_batched: X with L L^T X = B.
+
+    L: as returned by potrf_batched (same layout and interleave; only the
+    lower triangle is read; a failed factorization, all +0.0, gives X =
+    +0.0); B: [batch, n, nrhs] ("row") or [batch, nrhs, n] ("col").  Returns
+    X shaped like B.  Does not synchronize."""
+    torch = _torch()
+    _check_pair(torch, L, B, "L", "B")
+    nb, n, nrhs = _dims(L, B, layout, interleave, batch)
+    X = torch.empty_like(B) if out is None else out
+    s = stream if stream is not None else torch.cuda.current_stream(L.device)
+    dt = _dtype_code(torch, L)
+    with torch.cuda.device(L.device):
+        if interleave > 1:
+            rc = tdls_potrs_batched_ex(dt, _LAYOUTS[layout], n, nrhs, nb, _options(0, interleave),
+                                       L.data_ptr(), B.data_ptr(), X.data_ptr(), s.cuda_stream)
+        else:
+            rc = tdls_potrs_batched(dt, _LAYOUTS[layout], n, nrhs, nb, L.data_ptr(), B.data_ptr(),
+                                    X.data_ptr(), s.cuda_stream)
+    if rc != 0:
+        raise TdlsError(rc, "tdls_potrs_batched")
+    return X
 
 
 def posv_batched(A, B, layout: str = "row", shift: float = 0.0, out=None, stream=None,

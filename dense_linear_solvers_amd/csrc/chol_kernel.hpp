@@ -91,13 +91,15 @@ __device__ __forceinline__ float sqrt_ieee(float v) { return __builtin_sqrtf(v);
 
 // FACT = false: posv, X receives the solutions.  FACT = true: potrf (NRHS
 // must be 1, Bm is not read), X receives L in the layout of A, zero above
-// the diagonal.
-template <typename Real, int N, int NRHS, int T, bool FACT>
+// the diagonal.  SOLVE = true: potrs, A holds L as potrf writes it, X
+// receives the solutions, info is not written.
+template <typename Real, int N, int NRHS, int T, bool FACT, bool SOLVE = false>
 __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     chol_kernel(int col, int n, int nrhs, int64_t batch, Real shift, const Real* __restrict__ A,
                 const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ info,
                 int64_t ilv) {
   static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
+  static_assert(!(FACT && SOLVE), "potrs solves from given factors");
   using S = CholShape<Real, N, NRHS, T>;
   constexpr int R = S::R;
   constexpr int G = S::G;
@@ -120,7 +122,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   // the factorization (it plays no part in it), which keeps its registers
   // free meanwhile (n = 64 with 8: 171 -> 161 VGPRs, a third wave per SIMD);
   // smaller groups keep their occupancy either way and load it up front.
-  constexpr bool LATE_B = !FACT && NRHS > 1 && T == 64;
+  constexpr bool LATE_B = !FACT && !SOLVE && NRHS > 1 && T == 64;
   Real a[R][N];
   Real y[R][NRHS];
   {
@@ -175,153 +177,180 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
   }
 
-  // ---- exact symmetry: CH rows at a time (lanes of one slot) go to LDS,
-  // and every lane compares its row q with column q of the chunk
-  int asym = 0;   // a lane value, settled per chunk (see below)
-  sfor<0, (N + S::CH - 1) / S::CH>([&](auto cic) {
-    constexpr int r0 = decltype(cic)::value * S::CH;
-    constexpr int KC = r0 / T;                  // the slot holding rows r0 .. r0+CH-1
-    constexpr int t0 = r0 - KC * T;             // and the first lane
-    if (tx >= t0 && tx < t0 + S::CH && tx + KC * T < N) {
-      sfor<0, N>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        sq[(tx - t0) * ST + c] = a[KC][c];
-      });
-    }
-    wave_sync_lds();
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      const int qq = q < N ? q : N - 1;
-      sfor<0, S::CH>([&](auto rc) {
-        constexpr int r = r0 + decltype(rc)::value;
-        if constexpr (r < N)
-          asym |= (int)((q < N) & !(sq[(r - r0) * ST + qq] == a[K][r]));   // phantom rows excluded
-      });
-    });
-    // settled now: left to the end, every comparison's lane mask stays live
-    // in scalar registers
-    asm volatile("" : "+v"(asym));
-    wave_sync_lds();   // the chunk is rewritten next
-  });
-  // Status, in the ruSOLVER contract's order of precedence: -1 for a
-  // non-finite input entry, -2 for a matrix that is not symmetric, the
-  // first step whose pivot is not > 0 (j + 1), then -3 when a computed value
-  // is not finite: a diagonal entry of L (nf), an entry of x, or an entry of
-  // L.  A non-finite value never turns finite again in the updates that
-  // follow, so a non-finite entry of L shows in x.
-  int status;
-  {
-    bool inbad = false;
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      sfor<0, N>([&](auto cc) { inbad |= not_finite(a[K][decltype(cc)::value]); });
-      sfor<0, NRHS>([&](auto jc) { inbad |= not_finite(y[K][decltype(jc)::value]); });
-    });
-    // one status per group: any lane of the group that saw a non-finite
-    // entry, else a mismatch
-    status = group_any<T>(inbad, g * T) ? -1 : (group_any<T>(asym != 0, g * T) ? -2 : 0);
-  }
-  int nf = 0;   // a lane flag, settled at each step (asm barrier below)
-
-  // ---- the explicit diagonal shift, added once to A(q,q)
-  if (shift != Real(0)) {
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      const int q = tx + K * T;
-      sfor<0, N>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        if constexpr (c >= K * T && c < (K + 1) * T)
-          a[K][c] = (q == c && q < n) ? a[K][c] + shift : a[K][c];
-      });
-    });
-  }
-
-  // ---- factorization with the forward substitution folded in
-  sfor<0, N>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int js = j / T;
-    constexpr int jl = j % T;
-    constexpr int BL = T == 64 ? jl : jl % SL;   // lane of row j in the broadcast domain
-    const Real s = group_bcast<T, BL>(a[js][j]);
-    const bool bad = !(s > Real(0));
-    if (bad && status == 0) status = j + 1;
-    asm volatile("" : "+v"(status));   // settled now, not at the store
-    const Real d = bad ? Real(1) : sqrt_ieee(s);
-    nf |= not_finite(d);
-    asm volatile("" : "+v"(nf));
-    // multipliers of the rows below j; row j itself takes d
-    Real lm[R];
-    sfor<0, R>([&](auto Kc) {
-      constexpr int K = decltype(Kc)::value;
-      if constexpr (K < js) {
-        lm[K] = Real(0);
-      } else {
-        const Real l = a[K][j] / d;
-        if constexpr (K > js) {
-          lm[K] = l;
-          a[K][j] = l;
-        } else {
-          lm[K] = tx > jl ? l : Real(0);
-          a[K][j] = tx > jl ? l : (tx == jl ? d : a[K][j]);
-        }
-        asm volatile("" : "+v"(a[K][j]));
-      }
-    });
-    // forward substitution (one right-hand side: folded into the steps):
-    // y_j / d on its lane, then y_j leaves the rows below
-    sfor<0, NRHS>([&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      if constexpr (!FACT && NRHS == 1) {
-        const Real yj = y[js][r] / d;
-        y[js][r] = tx == jl ? yj : y[js][r];
-        const Real yb = group_bcast<T, BL>(y[js][r]);
+  int status = 0;
+  int nf = 0;                  // a lane flag, settled at each step (asm barrier below)
+  bool given_failed = false;   // potrs: the factor of a failed factorization
+  if constexpr (SOLVE) {
+    // ---- potrs: the rows hold L as potrf writes it (the entries above the
+    // diagonal are never read).  A failed factorization leaves L all +0.0,
+    // so L(0,0) == 0 marks it.  With one right-hand side L y = b runs here,
+    // step by step exactly as the factorization's folded forward
+    // substitution; with several, in the column-class solve below.
+    given_failed = group_bcast<T, 0>(a[0][0]) == Real(0);
+    if constexpr (NRHS == 1) {
+      sfor<0, N>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int js = j / T;
+        constexpr int jl = j % T;
+        constexpr int BL = T == 64 ? jl : jl % SL;
+        const Real d = group_bcast<T, BL>(a[js][j]);
+        const Real yj = y[js][0] / d;
+        y[js][0] = tx == jl ? yj : y[js][0];
+        const Real yb = group_bcast<T, BL>(y[js][0]);
         sfor<js, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          y[K][r] = __builtin_fma(-lm[K], yb, y[K][r]);
-        });
-      }
-    });
-    // rank-1 update of the columns right of j, on the slots holding rows at
-    // or below each column; L(c, j) comes from lane c % T, slot c / T.  A
-    // whole-wave group stages the column through LDS so that every 16-lane
-    // row holds the entries it serves, then broadcasts by DPP inside the
-    // fused multiply-add (instead of two readlanes per entry).
-    if constexpr (T == 64) {
-      static_assert(R == 1, "one row per lane in whole-wave groups");
-      if (tx > j && tx < N) sq[tx] = a[0][j];
-      wave_sync_lds();
-      constexpr int NU = (N + 15) / 16;
-      constexpr int U0 = (j + 1) / 16;
-      // one 16-entry block at a time keeps one source register live
-      sfor<U0, NU>([&](auto rc) {
-        constexpr int r = decltype(rc)::value;
-        const Real uc = sq[r * 16 + (tx & 15)];
-        constexpr int c0 = r * 16 > j + 1 ? r * 16 : j + 1;
-        constexpr int c1 = (r + 1) * 16 < N ? (r + 1) * 16 : N;
-        sfor<c0, c1>([&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-          fnmac_bcast<T, c % 16, c == c0>(a[0][c], uc, lm[0]);
+          const Real l = K > js ? a[K][j] : (tx > jl ? a[K][j] : Real(0));
+          y[K][0] = __builtin_fma(-l, yb, y[K][0]);
         });
       });
-      wave_sync_lds();   // read before the next column is written
     }
-    if constexpr (T != 64) sfor<j + 1, N>([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      constexpr int cs = c / T;
-      constexpr int cl = c % T;
-      if constexpr (T <= 16) {
-        sfor<cs, R>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          // the first read of each source register after its write above
-          // needs the DPP wait states
-          if constexpr (K >= js)
-            fnmac_bcast<T, cl % SL, K == cs && (c == j + 1 || cl == 0)>(a[K][c], a[cs][j],
-                                                                        lm[K]);
+  } else {
+    // ---- exact symmetry: CH rows at a time (lanes of one slot) go to LDS,
+    // and every lane compares its row q with column q of the chunk
+    int asym = 0;   // a lane value, settled per chunk (see below)
+    sfor<0, (N + S::CH - 1) / S::CH>([&](auto cic) {
+      constexpr int r0 = decltype(cic)::value * S::CH;
+      constexpr int KC = r0 / T;                  // the slot holding rows r0 .. r0+CH-1
+      constexpr int t0 = r0 - KC * T;             // and the first lane
+      if (tx >= t0 && tx < t0 + S::CH && tx + KC * T < N) {
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          sq[(tx - t0) * ST + c] = a[KC][c];
         });
       }
+      wave_sync_lds();
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        const int qq = q < N ? q : N - 1;
+        sfor<0, S::CH>([&](auto rc) {
+          constexpr int r = r0 + decltype(rc)::value;
+          if constexpr (r < N)
+            asym |= (int)((q < N) & !(sq[(r - r0) * ST + qq] == a[K][r]));   // phantom rows excluded
+        });
+      });
+      // settled now: left to the end, every comparison's lane mask stays live
+      // in scalar registers
+      asm volatile("" : "+v"(asym));
+      wave_sync_lds();   // the chunk is rewritten next
     });
-  });
+    // Status, in the ruSOLVER contract's order of precedence: -1 for a
+    // non-finite input entry, -2 for a matrix that is not symmetric, the
+    // first step whose pivot is not > 0 (j + 1), then -3 when a computed value
+    // is not finite: a diagonal entry of L (nf), an entry of x, or an entry of
+    // L.  A non-finite value never turns finite again in the updates that
+    // follow, so a non-finite entry of L shows in x.
+    {
+      bool inbad = false;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        sfor<0, N>([&](auto cc) { inbad |= not_finite(a[K][decltype(cc)::value]); });
+        sfor<0, NRHS>([&](auto jc) { inbad |= not_finite(y[K][decltype(jc)::value]); });
+      });
+      // one status per group: any lane of the group that saw a non-finite
+      // entry, else a mismatch
+      status = group_any<T>(inbad, g * T) ? -1 : (group_any<T>(asym != 0, g * T) ? -2 : 0);
+    }
+
+    // ---- the explicit diagonal shift, added once to A(q,q)
+    if (shift != Real(0)) {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (c >= K * T && c < (K + 1) * T)
+            a[K][c] = (q == c && q < n) ? a[K][c] + shift : a[K][c];
+        });
+      });
+    }
+
+    // ---- factorization with the forward substitution folded in
+    sfor<0, N>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int js = j / T;
+      constexpr int jl = j % T;
+      constexpr int BL = T == 64 ? jl : jl % SL;   // lane of row j in the broadcast domain
+      const Real s = group_bcast<T, BL>(a[js][j]);
+      const bool bad = !(s > Real(0));
+      if (bad && status == 0) status = j + 1;
+      asm volatile("" : "+v"(status));   // settled now, not at the store
+      const Real d = bad ? Real(1) : sqrt_ieee(s);
+      nf |= not_finite(d);
+      asm volatile("" : "+v"(nf));
+      // multipliers of the rows below j; row j itself takes d
+      Real lm[R];
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        if constexpr (K < js) {
+          lm[K] = Real(0);
+        } else {
+          const Real l = a[K][j] / d;
+          if constexpr (K > js) {
+            lm[K] = l;
+            a[K][j] = l;
+          } else {
+            lm[K] = tx > jl ? l : Real(0);
+            a[K][j] = tx > jl ? l : (tx == jl ? d : a[K][j]);
+          }
+          asm volatile("" : "+v"(a[K][j]));
+        }
+      });
+      // forward substitution (one right-hand side: folded into the steps):
+      // y_j / d on its lane, then y_j leaves the rows below
+      sfor<0, NRHS>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (!FACT && NRHS == 1) {
+          const Real yj = y[js][r] / d;
+          y[js][r] = tx == jl ? yj : y[js][r];
+          const Real yb = group_bcast<T, BL>(y[js][r]);
+          sfor<js, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            y[K][r] = __builtin_fma(-lm[K], yb, y[K][r]);
+          });
+        }
+      });
+      // rank-1 update of the columns right of j, on the slots holding rows at
+      // or below each column; L(c, j) comes from lane c % T, slot c / T.  A
+      // whole-wave group stages the column through LDS so that every 16-lane
+      // row holds the entries it serves, then broadcasts by DPP inside the
+      // fused multiply-add (instead of two readlanes per entry).
+      if constexpr (T == 64) {
+        static_assert(R == 1, "one row per lane in whole-wave groups");
+        if (tx > j && tx < N) sq[tx] = a[0][j];
+        wave_sync_lds();
+        constexpr int NU = (N + 15) / 16;
+        constexpr int U0 = (j + 1) / 16;
+        // one 16-entry block at a time keeps one source register live
+        sfor<U0, NU>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          const Real uc = sq[r * 16 + (tx & 15)];
+          constexpr int c0 = r * 16 > j + 1 ? r * 16 : j + 1;
+          constexpr int c1 = (r + 1) * 16 < N ? (r + 1) * 16 : N;
+          sfor<c0, c1>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            fnmac_bcast<T, c % 16, c == c0>(a[0][c], uc, lm[0]);
+          });
+        });
+        wave_sync_lds();   // read before the next column is written
+      }
+      if constexpr (T != 64) sfor<j + 1, N>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int cs = c / T;
+        constexpr int cl = c % T;
+        if constexpr (T <= 16) {
+          sfor<cs, R>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            // the first read of each source register after its write above
+            // needs the DPP wait states
+            if constexpr (K >= js)
+              fnmac_bcast<T, cl % SL, K == cs && (c == j + 1 || cl == 0)>(a[K][c], a[cs][j],
+                                                                          lm[K]);
+          });
+        }
+      });
+    });
+  }
 
   if constexpr (LATE_B) {
     // the right-hand sides, and their part of the input check (-1 outranks
@@ -394,12 +423,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       if (tx == 0) info[sys] = status;
     }
   } else {
-    const bool failed = status != 0 || nf != 0;
+    const bool failed = SOLVE ? given_failed : (status != 0 || nf != 0);
     bool xbad = false;
     if constexpr (NRHS == 1) {
       // ---- L^T x = y with the solver of the LU path: U = L^T, so lane c
       // writes L(c, q) into row q of the triangular store for every q <= c
-      xbad = upper_solve_store<Real, N, NRHS, T>(
+      // (potrs has no status: non-finite entries of x are kept)
+      xbad = upper_solve_store<Real, N, NRHS, T, !SOLVE>(
           sq, tx, (int)(g * T), live, failed, live ? sys : 0, n, nrhs, col, ilv, X,
           [&](Real* yt) {
             sfor<0, R>([&](auto Kc) {
@@ -543,7 +573,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       xbad = group_any<T>(bad, gb);
       if (live) {
         Real* Xs = X + sys_start(sys, ilv, (int64_t)n * nrhs);
-        const bool zero = failed || xbad;
+        const bool zero = failed || (!SOLVE && xbad);
         sfor<0, QR>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
           const int q = ph + P * m;
@@ -562,8 +592,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       }
     }
     if (status == 0 && (nf != 0 || xbad)) status = -3;
-    if (live) {
-      if (tx == 0) info[sys] = status;
+    if constexpr (!SOLVE) {
+      if (live && tx == 0) info[sys] = status;
     }
   }
 }

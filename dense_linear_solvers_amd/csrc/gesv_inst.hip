@@ -53,7 +53,7 @@ static int launch_getrs(const LaunchPlan& p, const void* LU, const void* B, void
   return (int)hipGetLastError();
 }
 
-template <typename Real, int N, int NRHS, int T, bool FACT>
+template <typename Real, int N, int NRHS, int T, bool FACT, bool SOLVE = false>
 static int launch_chol(const LaunchPlan& p, const void* A, const void* B, void* X,
                        int32_t* info, hipStream_t stream) {
   if constexpr (T == 32) {
@@ -64,7 +64,7 @@ static int launch_chol(const LaunchPlan& p, const void* A, const void* B, void* 
                   "host and device LDS sizes disagree");
     static_assert(S::BLOCK_BYTES <= 65536, "Cholesky LDS stays within the default limit");
     if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((chol_kernel<Real, N, NRHS, T, FACT>), dim3((unsigned)p.grid),
+    hipLaunchKernelGGL((chol_kernel<Real, N, NRHS, T, FACT, SOLVE>), dim3((unsigned)p.grid),
                        dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
                        p.batch, (Real)p.shift, static_cast<const Real*>(A),
                        static_cast<const Real*>(B), static_cast<Real*>(X), info, p.interleave);
@@ -92,6 +92,8 @@ static int launch_op(const LaunchPlan& p, const void* in0, const void* in1, void
         return (int)hipErrorInvalidConfiguration;
     case kOpPosv:
       return launch_chol<Real, N, NRHS, T, false>(p, in0, in1, out, info, stream);
+    case kOpPotrs:
+      return launch_chol<Real, N, NRHS, T, false, true>(p, in0, in1, out, nullptr, stream);
     default:
       return (int)hipErrorInvalidConfiguration;
   }

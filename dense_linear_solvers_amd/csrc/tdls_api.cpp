@@ -98,7 +98,8 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   p->flags = 0;
   p->interleave = 1;
   p->lds_bytes = op == kOpGetrs                    ? getrs_lds_bytes(N, NRHS, T, is64)
-                 : (op == kOpPotrf || op == kOpPosv) ? chol_lds_bytes(N, NRHS, T, is64)
+                 : (op == kOpPotrf || op == kOpPosv || op == kOpPotrs)
+                     ? chol_lds_bytes(N, NRHS, T, is64)
                                                      : gesv_lds_bytes(N, NRHS, T, is64);
   return 0;
 }
@@ -176,7 +177,7 @@ int tdls_plan_gesv(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_
 int tdls_plan_op(tdls_op op, tdls_dtype dtype, tdls_layout layout, int n, int nrhs,
                  int64_t batch, tdls_plan* out) {
   if (op != TDLS_OP_GESV && op != TDLS_OP_GETRF && op != TDLS_OP_GETRS && op != TDLS_OP_POTRF &&
-      op != TDLS_OP_POSV)
+      op != TDLS_OP_POSV && op != TDLS_OP_POTRS)
     return -1;
   tdls::LaunchPlan p;
   const bool factor = op == TDLS_OP_GETRF || op == TDLS_OP_POTRF;
@@ -323,6 +324,26 @@ int potrf_call(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch, doubl
   return tdls::launch(p, A, nullptr, L, nullptr, info, stream);
 }
 
+int potrs_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+               const Extra& x, const void* L, const void* B, void* X, hipStream_t stream) {
+  tdls::LaunchPlan p;
+  int rc = tdls::make_plan(tdls::kOpPotrs, (int)dtype, (int)layout, n, nrhs, batch, &p);
+  if (rc != 0) return rc;
+  if (batch == 0) return TDLS_SUCCESS;
+  p.interleave = x.ilv;
+  const int po = x.po;
+
+  const size_t es = dtype == TDLS_F64 ? 8 : 4;
+  const size_t bytesL = span(batch, x.ilv, (int64_t)n * n, es);
+  const size_t bytesB = span(batch, x.ilv, (int64_t)n * nrhs, es);
+  if (L == nullptr || tdls::misaligned(L, es)) return -6 - po;
+  if (B == nullptr || tdls::misaligned(B, es)) return -7 - po;
+  if (X == nullptr || tdls::misaligned(X, es) || tdls::overlaps(X, bytesB, L, bytesL) ||
+      tdls::overlaps(X, bytesB, B, bytesB))
+    return -8 - po;
+  return tdls::launch(p, L, B, X, nullptr, nullptr, stream);
+}
+
 int posv_call(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
               double shift, const Extra& x, const void* A, const void* B, void* X,
               int32_t* info, hipStream_t stream) {
@@ -418,6 +439,20 @@ int tdls_potrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t b
   if (tdls::bad_options(opt, 0u, batch)) return -6;
   return tdls::potrf_call(dtype, layout, n, batch, shift, tdls::extra_of(opt), A, L, info,
                           stream);
+}
+
+int tdls_potrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                       const void* L, const void* B, void* X, hipStream_t stream) {
+  return tdls::potrs_call(dtype, layout, n, nrhs, batch, tdls::Extra(), L, B, X, stream);
+}
+
+int tdls_potrs_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                          const tdls_options* opt, const void* L, const void* B, void* X,
+                          hipStream_t stream) {
+  const int rc = tdls::check_scalars((int)dtype, (int)layout, n, nrhs, batch);
+  if (rc != 0) return rc;
+  if (tdls::bad_options(opt, 0u, batch)) return -6;
+  return tdls::potrs_call(dtype, layout, n, nrhs, batch, tdls::extra_of(opt), L, B, X, stream);
 }
 
 int tdls_posv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,

@@ -42,7 +42,14 @@ constexpr int kWavesPerBlock = 1;
 constexpr uint32_t kFlagScaleMaxAbs = 1u;
 
 // Operations the library launches.
-enum OpKind : int { kOpGesv = 0, kOpGetrf = 1, kOpGetrs = 2, kOpPotrf = 3, kOpPosv = 4 };
+enum OpKind : int {
+  kOpGesv = 0,
+  kOpGetrf = 1,
+  kOpGetrs = 2,
+  kOpPotrf = 3,
+  kOpPosv = 4,
+  kOpPotrs = 5
+};
 
 // Everything a launch needs, decided on the host before any launch.
 struct LaunchPlan {

@@ -56,7 +56,8 @@ typedef enum tdls_op {
   TDLS_OP_GETRF = 1, /* factor only (tdls_getrf_batched) */
   TDLS_OP_GETRS = 2, /* solve from factors (tdls_getrs_batched) */
   TDLS_OP_POTRF = 3, /* Cholesky factor (tdls_potrf_batched) */
-  TDLS_OP_POSV = 4   /* Cholesky factor and solve (tdls_posv_batched) */
+  TDLS_OP_POSV = 4,  /* Cholesky factor and solve (tdls_posv_batched) */
+  TDLS_OP_POTRS = 5  /* solve from Cholesky factors (tdls_potrs_batched) */
 } tdls_op;
 
 /* Return codes of the calls (not the per-system status, see `info`). */
@@ -241,6 +242,30 @@ int tdls_potrf_batched(tdls_dtype dtype, tdls_layout layout, int n, int64_t batc
                        const void* A, void* L, int32_t* info, hipStream_t stream);
 
 /*
+ * Solve (L_s L_s^T) X_s = B_s from factors written by tdls_potrf_batched
+ * (LAPACK's potrs, lower): L y = b, each y_j = y_j / L(j,j) by IEEE division
+ * and removed from the rows below, then L^T x = y, each x_j = y_j / L(j,j)
+ * removed from the rows above, every step a fused multiply-add, in the order
+ * of tdls_posv_batched, so potrf then potrs gives posv's bits
+ * ("ruSOLVER：小矩阵 kernel 优化（实验性）", section on the unchanged numerical
+ * and failure contract: a failed system's factors are all zero, so a system
+ * whose L(0,0) is 0 gets X = +0.0).
+ *
+ * Arguments (-i on rejection):
+ *   [1] dtype, [2] layout, [3] n (1..64), [4] nrhs (1..8), [5] batch.
+ *   [6] L       device, batch * n * n elements, layout of A; only the
+ *               entries on and below the diagonal are read.  Read only.
+ *   [7] B       device, read only.
+ *   [8] X       device, like B; written; must not overlap L or B.
+ *       stream  HIP stream.
+ * No status: a zero or non-finite entry of L (other than a failed factor)
+ * gives non-finite entries of X.  Ownership, stream semantics and errors as
+ * for tdls_gesv_batched.
+ */
+int tdls_potrs_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                       const void* L, const void* B, void* X, hipStream_t stream);
+
+/*
  * Solve (A_s + shift I) X_s = B_s by Cholesky (LAPACK's posv): the
  * factorization of tdls_potrf_batched with L y = b folded into its steps,
  * then L^T x = y, each x_j = y_j / L(j,j) by IEEE division and removed from
@@ -340,6 +365,17 @@ int tdls_getrs_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs,
 int tdls_potrf_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int64_t batch,
                           double shift, const tdls_options* opt, const void* A, void* L,
                           int32_t* info, hipStream_t stream);
+
+/*
+ * tdls_potrs_batched with options (opt may be NULL; no flags): the batch
+ * interleave applies to L, B and X.
+ *
+ * Arguments: [1]..[5] as for tdls_potrs_batched, [6] opt, [7] L, [8] B,
+ * [9] X, stream.
+ */
+int tdls_potrs_batched_ex(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int64_t batch,
+                          const tdls_options* opt, const void* L, const void* B, void* X,
+                          hipStream_t stream);
 
 /*
  * tdls_posv_batched with options (opt may be NULL; no flags): the batch

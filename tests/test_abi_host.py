@@ -319,3 +319,28 @@ def test_interleaved_spans_and_ex_numbering(lib):
     assert v(0.0, Opt(0, 0, W), a, roomy, x, 0) == -11
     # an empty batch launches nothing, whatever the interleave
     assert tdls.tdls_posv_batched_ex(1, 0, n, 1, 0, 0.0, Opt(0, 0, 9), 0, 0, 0, 0, 0) == 0
+
+
+def test_potrs_validation_before_launch(lib):
+    n, nrhs, batch = 16, 2, 10
+    es = 8
+    l = 1 << 40                                  # never dereferenced: every call fails
+    b = l + batch * n * n * es                   # before the device is queried
+    x = b + batch * n * nrhs * es
+    f = lambda *p: tdls.tdls_potrs_batched(tdls.F64, tdls.ROW_MAJOR, n, nrhs, batch, *p, 0)
+    assert tdls.tdls_potrs_batched(5, 0, n, nrhs, batch, l, b, x, 0) == -1
+    assert tdls.tdls_potrs_batched(0, 0, n, 9, batch, l, b, x, 0) == -4
+    assert tdls.tdls_potrs_batched(0, 0, n, 1, 0, 0, 0, 0, 0) == 0     # empty batch
+    assert f(0, b, x) == -6
+    assert f(l + 4, b, x) == -6
+    assert f(l, 0, x) == -7
+    assert f(l, b, l) == -8                      # X overlaps L
+    assert f(l, b, b + 8) == -8                  # X overlaps B
+    Opt = tdls.Options
+    g = lambda opt, *p: tdls.tdls_potrs_batched_ex(tdls.F64, tdls.COL_MAJOR, n, nrhs, batch, opt,
+                                                   *p, 0)
+    assert g(Opt(1, 0, 1), l, b, x) == -6        # no scaling option for potrs
+    assert g(Opt(0, 0, 4), 0, b, x) == -7
+    assert g(Opt(0, 0, 4), l, b, l) == -9
+    p = tdls.plan_op("potrs", "f64", "row", 32, 3, 1000)
+    assert p == tdls.plan_op("posv", "f64", "row", 32, 3, 1000)

@@ -30,6 +30,10 @@ def test_algorithmic_bytes_and_flops_by_hand():
     assert bench.algorithmic_flops(2, 1, "gesv") == 3 + 6
     # Cholesky 2 x 2: sqrt, division, multiply-add, sqrt = 1 + 1 + 2 + 1
     assert bench.algorithmic_flops(2, 1, "potrf") == 5
+    # its solves divide in both substitutions: 2 x (2 divisions + 1 multiply-add)
+    assert bench.algorithmic_flops(2, 1, "potrs") == 8
+    assert bench.algorithmic_flops(2, 1, "posv") == 13
+    assert bench.algorithmic_bytes(2, 1, 8, "potrs") == 32 + 32
     # the headline: 8,836 B and 23,344 flops per system
     assert bench.algorithmic_bytes(32, 1, 8, "gesv") == 8836
     assert bench.algorithmic_flops(32, 1, "gesv") == 23344

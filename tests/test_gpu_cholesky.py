@@ -47,6 +47,14 @@ def gpu_potrf(A_st, layout, shift=0.0):
     return L.cpu().numpy(), info.cpu().numpy()
 
 
+def gpu_potrs(L_st, B_st, layout):
+    L = torch.from_numpy(np.ascontiguousarray(L_st)).to(DEV)
+    B = torch.from_numpy(np.ascontiguousarray(B_st)).to(DEV)
+    X = tdls.potrs_batched(L, B, layout)
+    torch.cuda.synchronize()
+    return X.cpu().numpy()
+
+
 def gpu_posv(A_st, B_st, layout, shift=0.0):
     A = torch.from_numpy(np.ascontiguousarray(A_st)).to(DEV)
     B = torch.from_numpy(np.ascontiguousarray(B_st)).to(DEV)
@@ -69,6 +77,7 @@ def check(A_l, B_l, layout, shift=0.0, what=""):
     A_st = oracle.to_storage(A_l, layout)
     B_st = oracle.rhs_to_storage(B_l, layout)
     Lg, ig = gpu_potrf(A_st, layout, shift)
+    Lg_st = Lg
     Lo, io = oracle.potrf(A_st, n, layout, shift)
     np.testing.assert_array_equal(ig, io, err_msg=f"{what}: potrf info")
     Lg = oracle.from_storage(Lg, layout, n)
@@ -82,6 +91,18 @@ def check(A_l, B_l, layout, shift=0.0, what=""):
     Xg, xg = gpu_posv(A_st, B_st, layout, shift)
     Xo, xo = oracle.posv(A_st, B_st, n, nrhs, layout, shift)
     np.testing.assert_array_equal(xg, xo, err_msg=f"{what}: posv info")
+    # potrs on the GPU's factors: posv's bits (same operations, same order),
+    # and the oracle's potrs on the same factors (failed ones give +0.0)
+    Xs = gpu_potrs(Lg_st, B_st, layout)
+    np.testing.assert_array_equal(Xs.view(np.uint8), Xg.view(np.uint8),
+                                  err_msg=f"{what}: potrf + potrs != posv")
+    Xso = oracle.potrs(Lg_st, B_st, n, nrhs, layout)
+    Xs_l = oracle.rhs_from_storage(Xs, layout, n, nrhs)
+    Xso_l = oracle.rhs_from_storage(Xso, layout, n, nrhs)
+    assert (Xs_l[~ok] == 0).all() and not np.signbit(Xs_l[~ok]).any(), what
+    if ok.any():
+        err = metrics.normwise_error(Xs_l[ok], Xso_l[ok])
+        assert err.max() <= parity.X_TOL[dt], f"{what}: potrs X error {err.max()}"
     Xg = oracle.rhs_from_storage(Xg, layout, n, nrhs)
     Xo = oracle.rhs_from_storage(Xo, layout, n, nrhs)
     assert (Xg[~ok] == 0).all() and not np.signbit(Xg[~ok]).any(), what
@@ -192,7 +213,8 @@ def test_group_size_does_not_change_results(monkeypatch):
             out = []
             for t in sizes:
                 monkeypatch.setenv("TDLS_GROUP_SIZE", str(t))
-                out.append(gpu_potrf(A, "row") + gpu_posv(A, B, "row"))
+                L, info = gpu_potrf(A, "row")
+                out.append((L, info) + gpu_posv(A, B, "row") + (gpu_potrs(L, B, "row"),))
             monkeypatch.delenv("TDLS_GROUP_SIZE")
             for t, o in zip(sizes[1:], out[1:]):
                 for u, v in zip(out[0], o):

@@ -1,6 +1,7 @@
 """GPU parity of interleaved batches (the *_ex calls with interleave W):
 arrays of structures of arrays (1 < W < batch, the last block ragged) and
-structures of arrays (W = batch) for gesv, getrf, getrs, potrf and posv.
+structures of arrays (W = batch) for gesv, getrf, getrs, potrf, potrs and
+posv.
 
 Bar: the outputs are bitwise those of the plain calls on the same systems
 (the arithmetic does not depend on where a system is stored; the plain
@@ -143,6 +144,11 @@ def test_interleaved_cholesky(case):
         np.testing.assert_array_equal(layouts.from_interleaved(Lh, batch), L0)
         np.testing.assert_array_equal(_host(finfo), f0)
         assert (layouts.padding_of(Lh, batch) == SENTINEL).all()
+        Xs = torch.full_like(Bi, SENTINEL)
+        tdls.potrs_batched(L, Bi, layout, out=Xs, interleave=W, batch=batch)
+        Xsh = _host(Xs)
+        np.testing.assert_array_equal(layouts.from_interleaved(Xsh, batch), X0)   # posv's bits
+        assert (layouts.padding_of(Xsh, batch) == SENTINEL).all()
     Xo, io = oracle.posv(A_st, B_st, n, nrhs, layout, shift=0.25)
     assert (io == i0).all()
     ok = io == 0
