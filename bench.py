@@ -43,15 +43,17 @@ DEFAULT_WORKLOAD = "n32_f64_col"
 def algorithmic_bytes(n: int, nrhs: int, es: int, op: str = "gesv") -> int:
     """Bytes the method must move per system.  gesv: A and B read once, X,
     piv and info written once.  getrf: A read once, LU, piv and info
-    written once.  getrs: LU, piv and B read once, X written once."""
+    written once.  getrs: LU, piv and B read once, X written once.
+    potrs reads only the lower triangle of L (the rest of the matrix is
+    never part of its input)."""
     if op == "getrf":
         return 2 * n * n * es + 4 * n + 4
     if op == "getrs":
         return n * n * es + 4 * n + 2 * n * nrhs * es
     if op == "potrf":                    # A read, L written, info
         return 2 * n * n * es + 4
-    if op == "potrs":                    # L, B read, X written
-        return n * n * es + 2 * n * nrhs * es
+    if op == "potrs":                    # L's lower triangle, B read, X written
+        return n * (n + 1) // 2 * es + 2 * n * nrhs * es
     if op == "posv":                     # A, B read, X, info written
         return n * n * es + 2 * n * nrhs * es + 4
     return n * n * es + 2 * n * nrhs * es + 4 * n + 4

@@ -140,7 +140,14 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           const Real* br = Bs + (COL ? qq : qq * NRHS);
           sfor<0, N>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
-            a[K][c] = ar[COL ? c * N : c];
+            if constexpr (!SOLVE)
+              a[K][c] = ar[COL ? c * N : c];
+            else if constexpr (c >= (K + 1) * T)   // above the diagonal on every lane
+              a[K][c] = Real(0);
+            else if (c <= q)                       // potrs reads L's lower triangle only
+              a[K][c] = ar[COL ? c * N : c];
+            else
+              a[K][c] = Real(0);
           });
           sfor<0, NRHS>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
@@ -164,7 +171,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         sfor<0, N>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           a[K][c] = (q == c) ? Real(1) : Real(0);
-          if (qrow && c < n) a[K][c] = As[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
+          if (qrow && c < n && (!SOLVE || c <= q))
+            a[K][c] = As[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
         });
         sfor<0, NRHS>([&](auto jc) {
           constexpr int j = decltype(jc)::value;

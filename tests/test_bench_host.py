@@ -33,7 +33,8 @@ def test_algorithmic_bytes_and_flops_by_hand():
     # its solves divide in both substitutions: 2 x (2 divisions + 1 multiply-add)
     assert bench.algorithmic_flops(2, 1, "potrs") == 8
     assert bench.algorithmic_flops(2, 1, "posv") == 13
-    assert bench.algorithmic_bytes(2, 1, 8, "potrs") == 32 + 32
+    # potrs reads L's lower triangle (3 entries of a 2 x 2), B, and writes X
+    assert bench.algorithmic_bytes(2, 1, 8, "potrs") == 24 + 32
     # the headline: 8,836 B and 23,344 flops per system
     assert bench.algorithmic_bytes(32, 1, 8, "gesv") == 8836
     assert bench.algorithmic_flops(32, 1, "gesv") == 23344

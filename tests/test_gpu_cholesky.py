@@ -96,6 +96,14 @@ def check(A_l, B_l, layout, shift=0.0, what=""):
     Xs = gpu_potrs(Lg_st, B_st, layout)
     np.testing.assert_array_equal(Xs.view(np.uint8), Xg.view(np.uint8),
                                   err_msg=f"{what}: potrf + potrs != posv")
+    # only L's lower triangle is potrs's input: NaN above the diagonal
+    # changes no bit
+    Lp = oracle.from_storage(Lg_st, layout, n).copy()
+    iu = np.triu_indices(n, 1)
+    Lp[:, iu[0], iu[1]] = np.nan
+    Xp = gpu_potrs(oracle.to_storage(Lp, layout), B_st, layout)
+    np.testing.assert_array_equal(Xp.view(np.uint8), Xs.view(np.uint8),
+                                  err_msg=f"{what}: potrs read above the diagonal")
     Xso = oracle.potrs(Lg_st, B_st, n, nrhs, layout)
     Xs_l = oracle.rhs_from_storage(Xs, layout, n, nrhs)
     Xso_l = oracle.rhs_from_storage(Xso, layout, n, nrhs)
