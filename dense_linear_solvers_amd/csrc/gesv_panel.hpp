@@ -664,13 +664,74 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   });
 
   // ---- factorization, panel by panel
+  //
+  // Slot compaction.  Rows never move during the steps, so a lane's slots
+  // hold rows of any position and every slot takes part in every step.  At
+  // each slot boundary k0 = m*T (m >= 1, a panel boundary when B divides T)
+  // the rows of slots m-1 .. R-1 go through LDS and come back in position
+  // order: slot K then holds the positions K*T .. K*T+T-1, so slots below m
+  // hold only finished rows (positions < k0) and the steps and trailing
+  // updates from k0 on skip them at compile time.  Arithmetic is unchanged:
+  // a finished row takes only zero multipliers.
+  constexpr bool COMPACT = R > 1 && T % B == 0;
   constexpr int NP = (N + B - 1) / B;
   sfor<0, NP>([&](auto pc) {
     constexpr int k0 = decltype(pc)::value * B;
     constexpr int bw = (N - k0) < B ? (N - k0) : B;   // panel width
     constexpr int NT = N - k0 - bw;                    // trailing matrix columns
     constexpr int W = NT + NRHS;                       // trailing entries per row
+    constexpr int K0 = COMPACT ? k0 / T : 0;           // slots of finished rows only
     Real lm[B][R];                                     // multiplier, 0 unless below
+    if constexpr (COMPACT && k0 > 0 && k0 % T == 0) {
+      constexpr int KP = K0 - 1;                 // slots already in position order
+      constexpr int NS = N - KP * T;             // rows staged (positions KP*T .. N-1)
+      constexpr int E = N + (FACT ? 0 : NRHS);   // entries per row: columns, right-hand sides
+      // entries below EB are needed by no staged row: the solve keeps only U
+      // (columns from the row's position on), the factorization all of L\U
+      constexpr int EB = FACT ? 0 : KP * T;
+      // row stride in LDS: a multiple of the vector width, not of 32 banks
+      constexpr int CM = S::GROUP_ELEMS / NS / VEC * VEC;
+      constexpr int RS = ((CM * (int)sizeof(Real) / 4) % 32 == 0 && CM > VEC) ? CM - VEC : CM;
+      static_assert(RS >= VEC && NS * RS <= S::GROUP_ELEMS, "staging fits the group area");
+      constexpr int NCH = (E - EB + RS - 1) / RS;
+      auto ent = [&](auto Kc, auto ec) -> Real& {
+        constexpr int K = decltype(Kc)::value;
+        constexpr int e = decltype(ec)::value;
+        if constexpr (e < N) return a[K][e];
+        else return y[K][e - N];
+      };
+      sfor<0, NCH>([&](auto hc) {
+        constexpr int e0 = EB + decltype(hc)::value * RS;
+        constexpr int e1 = (e0 + RS) < E ? (e0 + RS) : E;
+        sfor<KP, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const int p = lab[K];
+          if (p >= 0) {
+            Real* dst = rec + (p - KP * T) * RS - e0;   // entry e at dst[e]
+            sfor<e0, e1>([&](auto ec) { dst[decltype(ec)::value] = ent(Kc, ec); });
+          }
+        });
+        wave_sync_lds();
+        sfor<KP, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          // first entry slot K needs: a finished slot its U part, an active
+          // one its trailing columns (the factorization: the whole row)
+          constexpr int es = FACT ? 0 : (K < K0 ? K * T : k0);
+          constexpr int b0 = e0 > es ? e0 : es;
+          if (K * T + T <= N || tx + K * T < N) {
+            const Real* src = rec + (tx + K * T - KP * T) * RS - e0;
+            sfor<b0, e1>([&](auto ec) { ent(Kc, ec) = src[decltype(ec)::value]; });
+          }
+        });
+        wave_sync_lds();
+      });
+      sfor<KP, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        lab[K] = q < N ? q : -1;
+        kb[K] = ((uint32_t)(q < N ? q : 0) << 13) | ((uint32_t)lane << 5) | (K << 1);
+      });
+    }
     if constexpr (k0 == 0) {
       // input check of the panel's own columns (the others below)
       sfor<0, R>([&](auto Kc) {
@@ -697,7 +758,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // exactly and the low word, then the lowest position, decide among
       // the lanes that hold the maximum.
       uint32_t hw[R], lw[R], hf[R];
-      sfor<0, R>([&](auto Kc) {
+      sfor<K0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         if constexpr (is64) {
           hw[K] = hi_word(a[K][k]);
@@ -708,8 +769,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         }
         hf[K] = lab[K] >= k ? (hw[K] | 0x80000000u) : 0u;
       });
-      uint32_t lmax = hf[0];
-      sfor<1, R>([&](auto Kc) {
+      uint32_t lmax = hf[K0];
+      sfor<K0 + 1, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         lmax = lmax > hf[K] ? lmax : hf[K];
       });
@@ -719,7 +780,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       bool tp[R];
       uint64_t tmask = 0;
       int ntop = 0;
-      sfor<0, R>([&](auto Kc) {
+      sfor<K0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         tp[K] = hf[K] == mh;
         const uint64_t b = __builtin_amdgcn_ballot_w64(tp[K]);
@@ -729,9 +790,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // The lane's chosen slot (its top slot, or its best one when the
       // exact comparison runs): its key, value and entries right of k in the
       // panel are what the winning lane hands to its group.
-      uint32_t ch = hw[0], cl = lw[0], ck = kb[0];
+      uint32_t ch = hw[K0], cl = lw[K0], ck = kb[K0];
       Real cpan[PC > 0 ? PC : 1];
-      sfor<0, PC>([&](auto cc) { cpan[decltype(cc)::value] = a[0][k + 1 + decltype(cc)::value]; });
+      sfor<0, PC>([&](auto cc) { cpan[decltype(cc)::value] = a[K0][k + 1 + decltype(cc)::value]; });
       auto choose = [&](auto Kc, bool take) {
         constexpr int K = decltype(Kc)::value;
         ch = take ? hw[K] : ch;
@@ -744,7 +805,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       };
       int wl;   // winning lane
       if (__builtin_expect(ntop == G, 1)) {
-        sfor<1, R>([&](auto Kc) { choose(Kc, tp[decltype(Kc)::value]); });
+        sfor<K0 + 1, R>([&](auto Kc) { choose(Kc, tp[decltype(Kc)::value]); });
         if constexpr (T == 64) {
           wl = __builtin_ctzll(tmask);
         } else {
@@ -752,8 +813,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           wl = gbase + __builtin_ctz((uint32_t)(tmask >> gbase) & GM);
         }
       } else {
-        uint32_t bh = hf[0], bl = lw[0];
-        sfor<1, R>([&](auto Kc) {
+        uint32_t bh = hf[K0], bl = lw[K0];
+        sfor<K0 + 1, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
           bool take;
           if constexpr (is64) {
@@ -798,7 +859,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       const Real d = zero_pivot ? Real(1) : dpiv;
 
       // (c) logical interchange of positions k and p
-      sfor<0, R>([&](auto Kc) {
+      sfor<K0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int old = lab[K];
         const int nl = old == k ? p : (old == p ? k : old);
@@ -810,7 +871,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
 
       // (d) multipliers of the rows now below position k (IEEE division);
       // column k itself keeps its values (the U entries of the rows above)
-      sfor<0, R>([&](auto Kc) {
+      sfor<K0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const Real l = a[K][k] / d;
         lm[i][K] = lab[K] > k ? l : Real(0);
@@ -823,7 +884,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // column is complete when its search starts
       sfor<0, PC>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
-        sfor<0, R>([&](auto Kc) {
+        sfor<K0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
           a[K][k + 1 + c] = __builtin_fma(-lm[i][K], upan[c], a[K][k + 1 + c]);
         });
@@ -855,7 +916,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // The owner of each pivot row writes its record (exec-masked: an LDS
       // write costs the same whatever the number of active lanes), one
       // register (pair) per entry at a compile-time offset.
-      sfor<0, R>([&](auto Kc) {
+      sfor<K0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int j = lab[K] - k0;
         if (j >= 0 && j < bw) {
@@ -900,9 +961,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int m = decltype(mc)::value;
         constexpr int L = e % SL;
         constexpr int r = e / SL;
-        sfor<0, R>([&](auto Kc) {
+        sfor<K0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          constexpr bool first = (L == 0) && (K == 0);
+          constexpr bool first = (L == 0) && (K == K0);
           if constexpr (e < NT)
             fnmac_bcast<T, L, first>(a[K][k0 + bw + e], u[m][r], lm[m][K]);
           else
