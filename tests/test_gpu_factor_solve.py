@@ -207,7 +207,7 @@ def test_group_size_does_not_change_factors_or_solutions(monkeypatch):
     rng = np.random.default_rng(43)
     compared = 0
     for dtype in ("f32", "f64"):
-        for n, nrhs in ((8, 1), (16, 4), (24, 2), (32, 1), (32, 8)):
+        for n, nrhs in ((8, 1), (13, 3), (16, 4), (21, 1), (24, 2), (30, 2), (32, 1), (32, 8)):
             code = tdls.F64 if dtype == "f64" else tdls.F32
             sizes = []
             for t in (4, 16, 32, 64):
