@@ -652,16 +652,20 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   // of the factors.  A non-finite value never turns finite again in the
   // updates that follow, so a non-finite multiplier or U entry shows in x.
   int status = 0;
-  int inbad = 0;   // lane flags, settled where they are formed (asm barriers
-  int nf = 0;      // below): left to their use they keep values alive
-  // Per-slot key bits for the pivot search: position << 13 | lane << 5 |
-  // slot << 1 (the sign of the candidate goes in bit 0).  Positions are
-  // unique, so comparing keys compares positions.
-  uint32_t kb[R];
-  sfor<0, R>([&](auto Kc) {
+  int inbad = 0;   // a lane flag, settled where it is formed (asm barrier
+                   // below): left to its use it keeps values alive
+  // Non-finite pivots: every pivot enters pz as a fused multiply-add by
+  // zero, which leaves pz +0.0 unless a pivot is an infinity or a NaN (then
+  // pz is NaN for good); one instruction a step instead of a compare and a
+  // flag update.
+  Real pz = Real(0);
+  // Key of slot K for the exact pivot comparison: position << 13 | lane << 5
+  // | slot << 1.  Positions are unique, so comparing keys compares
+  // positions; keys are formed only when a group has a tie on the high word.
+  auto key = [&](auto Kc) -> uint32_t {
     constexpr int K = decltype(Kc)::value;
-    kb[K] = ((uint32_t)(lab[K] < 0 ? 0 : lab[K]) << 13) | ((uint32_t)lane << 5) | (K << 1);
-  });
+    return ((uint32_t)(lab[K] < 0 ? 0 : lab[K]) << 13) | ((uint32_t)lane << 5) | (K << 1);
+  };
 
   // ---- factorization, panel by panel
   //
@@ -729,7 +733,6 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
         lab[K] = q < N ? q : -1;
-        kb[K] = ((uint32_t)(q < N ? q : 0) << 13) | ((uint32_t)lane << 5) | (K << 1);
       });
     }
     if constexpr (k0 == 0) {
@@ -788,16 +791,17 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         ntop += __builtin_popcountll(b);
       });
       // The lane's chosen slot (its top slot, or its best one when the
-      // exact comparison runs): its key, value and entries right of k in the
-      // panel are what the winning lane hands to its group.
-      uint32_t ch = hw[K0], cl = lw[K0], ck = kb[K0];
+      // exact comparison runs): its position, value and entries right of k
+      // in the panel are what the winning lane hands to its group.
+      uint32_t ch = hw[K0], cl = lw[K0];
+      int cp = lab[K0];
       Real cpan[PC > 0 ? PC : 1];
       sfor<0, PC>([&](auto cc) { cpan[decltype(cc)::value] = a[K0][k + 1 + decltype(cc)::value]; });
       auto choose = [&](auto Kc, bool take) {
         constexpr int K = decltype(Kc)::value;
         ch = take ? hw[K] : ch;
         cl = take ? lw[K] : cl;
-        ck = take ? kb[K] : ck;
+        cp = take ? lab[K] : cp;
         sfor<0, PC>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           cpan[c] = take ? a[K][k + 1 + c] : cpan[c];
@@ -814,18 +818,21 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         }
       } else {
         uint32_t bh = hf[K0], bl = lw[K0];
+        uint32_t ck = key(std::integral_constant<int, K0>{});
         sfor<K0 + 1, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
+          const uint32_t kk = key(Kc);
           bool take;
           if constexpr (is64) {
             const uint64_t c = ((uint64_t)hf[K] << 32) | lw[K];
             const uint64_t bb = ((uint64_t)bh << 32) | bl;
-            take = (c > bb) | ((c == bb) & (kb[K] < ck));
+            take = (c > bb) | ((c == bb) & (kk < ck));
           } else {
-            take = (hf[K] > bh) | ((hf[K] == bh) & (kb[K] < ck));
+            take = (hf[K] > bh) | ((hf[K] == bh) & (kk < ck));
           }
           bh = take ? hf[K] : bh;
           bl = take ? lw[K] : bl;
+          ck = take ? kk : ck;
           choose(Kc, take);
         });
         bool top = bh == mh;
@@ -836,8 +843,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         const uint32_t kmin = group_reduce<T, false>(top ? ck : 0xffffffffu);
         wl = (int)((kmin >> 5) & 63u);
       }
-      const uint32_t wk = lane_fetch_u32<T>(ck, wl);      // winner's key
-      const int p = (int)(wk >> 13);
+      const int p = (int)lane_fetch_u32<T>((uint32_t)cp, wl);   // winner's position
       Real upan[PC > 0 ? PC : 1];                          // pivot row, right of k
       sfor<0, PC>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
@@ -850,8 +856,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       else
         dpiv = __builtin_bit_cast(float, lane_fetch_u32<T>(ch, wl));
       const bool zero_pivot = dpiv == Real(0);
-      nf |= not_finite(dpiv);
-      asm volatile("" : "+v"(nf));
+      pz = __builtin_fma(dpiv, Real(0), pz);
+      asm volatile("" : "+v"(pz));   // in place, not sunk to the end
       if (zero_pivot && status == 0) status = k + 1;
       // settle the status here: left to the end, the per-step zero flags of
       // every step stay live in scalar registers
@@ -864,7 +870,6 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         const int old = lab[K];
         const int nl = old == k ? p : (old == p ? k : old);
         lab[K] = nl;
-        kb[K] = (kb[K] & 0x1fffu) | ((uint32_t)(nl < 0 ? 0 : nl) << 13);
       });
       if (tx == kl) pv[ks] = p;
       asm volatile("" : "+v"(pv[ks]));   // likewise for the pivot record
@@ -979,6 +984,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     }
   });
 
+  const bool nf = pz != pz;   // a pivot was an infinity or a NaN
+
   if constexpr (FACT) {
     // ---- factors: every row, whatever lane holds it, is row lab of L\U
     // (multipliers before its position, U from it on); a failed system gets
@@ -994,7 +1001,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       });
     }
     {
-      bool bad = nf != 0;
+      bool bad = nf;
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = lab[K];
@@ -1054,7 +1061,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
     wave_sync_lds();  // the last records have been read
     const bool xbad = upper_solve_store<Real, N, NRHS, T>(
-        rec, tx, gbase, live, status != 0 || nf != 0, live ? sys : 0, n, nrhs, col, ilv, X,
+        rec, tx, gbase, live, status != 0 || nf, live ? sys : 0, n, nrhs, col, ilv, X,
         [&](Real* yt) {
           sfor<0, R>([&](auto Kc) {
             constexpr int K = decltype(Kc)::value;
@@ -1081,7 +1088,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           });
         });
 
-    if (status == 0 && (nf != 0 || xbad)) status = -3;
+    if (status == 0 && (nf || xbad)) status = -3;
     const bool failed = status != 0;
 
     // ---- piv (all -1 for a failed system) and info
