@@ -199,6 +199,19 @@ def test_spd_full_size_sampled():
     Xo = oracle.rhs_from_storage(Xo, w.layout, w.n, w.nrhs)
     err = metrics.normwise_error(Xg, Xo)
     assert err.max() <= parity.X_TOL[np.dtype(np.float64)]
+    # potrf and potrs over the whole batch, as the benchmark runs them:
+    # sampled factors against the oracle, and potrf then potrs gives posv's
+    # bits on every system
+    L, linfo = gpu_potrf(w.A, w.layout)
+    assert (linfo == 0).all()
+    Lo, lio = oracle.potrf(np.ascontiguousarray(w.A[idx]), w.n, w.layout)
+    assert (lio == 0).all()
+    Lg = oracle.from_storage(L[idx], w.layout, w.n).astype(np.float64)
+    # the oracle's L is logical (row-major) whatever the storage layout
+    rel = np.abs(Lg - Lo).max(axis=(1, 2)) / np.abs(Lo).max(axis=(1, 2))
+    assert rel.max() <= parity.X_TOL[np.dtype(np.float64)]
+    Xs = gpu_potrs(L, w.B, w.layout)
+    np.testing.assert_array_equal(Xs.view(np.uint8), X.view(np.uint8))
 
 
 def test_group_size_does_not_change_results(monkeypatch):
