@@ -75,6 +75,7 @@ int make_plan(int op, int dtype, int layout, int n, int nrhs, int64_t batch, Lau
   int T = T0;
   const int64_t waves0 = (batch + kWaveSize / T0 - 1) / (kWaveSize / T0);
   if (T1 > T0 && waves0 * (T1 / T0) <= kSimds) T = T1;   // small batch: more, shorter waves
+  if (lu_prefers_wider(op, N, is64, T0, T1)) T = T1;
   const int forced = group_size_override();
   if (forced != 0) {
     if (forced != T0 && (T1 == 0 || forced != T1)) return TDLS_ERR_NO_KERNEL;

@@ -104,6 +104,18 @@ constexpr int alt_group_size(int N, int NRHS, bool is64) {
   return (N <= 32 && t0 < 64) ? (t0 == 4 ? 16 : 64) : 0;
 }
 
+// The LU operations in float64 at N = 16 run the 16-lane group (one row per
+// lane) rather than the quad (four rows per lane, twice the registers of a
+// float32 row): measured on 65,536 and 1,048,576 systems, gesv 0.102 ->
+// 0.059 ms and 1.29 -> 0.95 ms (nrhs = 4), getrs 0.81 -> 0.62 ms, getrf
+// even.  The Cholesky kernels keep the quad (potrf 0.94 against 1.14 ms,
+// posv 0.68 against 1.07 ms at the larger batch); at N = 8 and in float32
+// the quad is ahead for every operation.
+constexpr bool lu_prefers_wider(int op, int N, bool is64, int T0, int T1) {
+  return is64 && N == 16 && T0 == 4 && T1 == 16 &&
+         (op == kOpGesv || op == kOpGetrf || op == kOpGetrs);
+}
+
 // Panel width of the factorization (columns whose pivot rows are exchanged
 // together through LDS).
 constexpr int panel_width(int N, [[maybe_unused]] int NRHS, [[maybe_unused]] bool is64) {

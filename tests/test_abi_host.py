@@ -344,3 +344,17 @@ def test_potrs_validation_before_launch(lib):
     assert g(Opt(0, 0, 4), l, b, l) == -9
     p = tdls.plan_op("potrs", "f64", "row", 32, 3, 1000)
     assert p == tdls.plan_op("posv", "f64", "row", 32, 3, 1000)
+
+
+def test_group_size_choice_per_op(lib):
+    """LU in float64 at n = 16 runs 16-lane groups at every batch size; the
+    Cholesky kernels and float32 keep 4-lane groups there (large batches)."""
+    big = 1 << 20
+    for n in (9, 16):
+        for op in ("getrf", "getrs"):
+            assert tdls.plan_op(op, "f64", "row", n, 1, big)["group_size"] == 16
+        assert tdls.plan_gesv("f64", "row", n, 4, big)["group_size"] == 16
+        for op in ("potrf", "posv", "potrs"):
+            assert tdls.plan_op(op, "f64", "row", n, 1, big)["group_size"] == 4
+        assert tdls.plan_gesv("f32", "row", n, 4, big)["group_size"] == 4
+    assert tdls.plan_gesv("f64", "row", 8, 1, big)["group_size"] == 4
