@@ -103,7 +103,27 @@ KERNEL_OF_OP = {"gesv": "gesv_panel_kernel", "getrf": "gesv_panel_kernel",
 
 
 def traffic_path(workload: str, op: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{op}_{workload}_traffic.json")
+    return os.path.join(ROOT, "profiles", f"{op}_{workload}_traffic.txt")
+
+
+TRAFFIC_MARKER = "# data (read by bench.py while kernel_source_hash matches the sources):"
+
+
+def traffic_lines(d: dict) -> list:
+    """The data lines of a traffic summary: ``key = value``, one a line."""
+    return [f"{k} = {v}" for k, v in d.items()]
+
+
+def read_traffic(path: str) -> dict:
+    """The ``key = value`` lines of a traffic summary (comments skipped)."""
+    d = {}
+    with open(path, encoding="utf-8") as fh:
+        for line in fh:
+            if line.startswith("#") or " = " not in line:
+                continue
+            k, v = line.rstrip("\n").split(" = ", 1)
+            d[k] = v
+    return d
 
 
 def measured_traffic(workload: str, op: str = "gesv"):
@@ -112,11 +132,11 @@ def measured_traffic(workload: str, op: str = "gesv"):
     path = traffic_path(workload, op)
     if not os.path.exists(path):
         return None
-    with open(path, encoding="utf-8") as fh:
-        d = json.load(fh)
+    d = read_traffic(path)
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    v = d.get("hbm_bytes_per_launch")
+    return float(v) if v is not None else None
 
 
 def _counter_values(csv_dir: str, counter: str, kernel_prefix: str) -> list:
@@ -155,9 +175,19 @@ def summarize_counters(workload: str, op: str, fetch_dir: str, write_dir: str,
          "fetch_scale": fetch_scale, "write_scale": write_scale,
          "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
          "hbm_bytes_per_launch": fetch_b + write_b}
+    # the summary's comment lines (commands, calibration, the figures in
+    # words) stay; the data lines below the marker are replaced
     out = traffic_path(workload, op)
+    head = [f"# HBM traffic of {kern} ({op}) on {workload}: rocprofv3 FETCH_SIZE and "
+            "WRITE_SIZE per dispatch, each scaled by the same counter on a plain copy",
+            TRAFFIC_MARKER]
+    if os.path.exists(out):
+        with open(out, encoding="utf-8") as fh:
+            old = fh.read().splitlines()
+        if TRAFFIC_MARKER in old:
+            head = old[:old.index(TRAFFIC_MARKER) + 1]
     with open(out, "w", encoding="utf-8") as fh:
-        json.dump(d, fh, indent=1)
+        fh.write("\n".join(head + traffic_lines(d)) + "\n")
         fh.write("\n")
     return d
 
@@ -263,7 +293,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                                                              "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="write profiles/<op>_<workload>_traffic.json from rocprofv3 --pmc "
+                    help="write the data lines of profiles/<op>_<workload>_traffic.txt from rocprofv3 --pmc "
                          "output directories (no GPU needed)")
     args = ap.parse_args()
     if args.summarize_counters:

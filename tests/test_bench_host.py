@@ -67,3 +67,25 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_traffic_summary_round_trip(tmp_path):
+    """The committed traffic summaries are text: comment lines, then
+    ``key = value`` data lines that bench.py reads back."""
+    d = {"workload": "w", "op": "gesv", "kernel_source_hash": "12e5abc",
+         "hbm_bytes_per_launch": 1234.5}
+    p = tmp_path / "t.txt"
+    p.write_text("# comment = not data\n" + bench.TRAFFIC_MARKER + "\n"
+                 + "\n".join(bench.traffic_lines(d)) + "\n")
+    r = bench.read_traffic(str(p))
+    assert r["kernel_source_hash"] == "12e5abc"          # kept as text
+    assert float(r["hbm_bytes_per_launch"]) == 1234.5
+    assert "comment" not in r
+    # every committed summary parses and names its workload and op
+    import glob
+    files = glob.glob(os.path.join(bench.ROOT, "profiles", "*_traffic.txt"))
+    assert files
+    for f in files:
+        r = bench.read_traffic(f)
+        assert os.path.basename(f) == f"{r['op']}_{r['workload']}_traffic.txt"
+        assert float(r["hbm_bytes_per_launch"]) > 0
