@@ -75,6 +75,57 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   unsigned char* glds = lds_raw + (wave * G + g) * S::GROUP_BYTES;
   int32_t* pl = reinterpret_cast<int32_t*>(glds);
 
+  // ---- load, in two parts: row q of L\U for each position q of the lane
+  // (past n the identity), and row src(q) of B (past n zero) once the pivot
+  // walk below has named it.  Source rows are clamped into the matrix, so a
+  // malformed pivot cannot address outside it.  With 16- and 64-lane groups
+  // L\U is loaded before the walk, which it does not depend on, so its
+  // latency overlaps the walk (n = 32 float64: 0.444 -> 0.413 ms, n = 64:
+  // 1.43 -> 1.39 ms); with quads (four rows per lane) the rows would stay
+  // live through the walk and cost occupancy (n = 16 float32: 0.0265 ->
+  // 0.031 ms), so there they follow it.
+  constexpr bool EARLY_LU = T >= 16;
+  Real a[R][N];
+  Real y[R][NRHS];
+  const bool exact = n == N && nrhs == NRHS && ilv == 1;
+  auto load_lu = [&]() {
+    const Real* Ls = LU + sys_start(live ? sys : 0, ilv, (int64_t)n * n);
+    if (exact) {
+      // the kernel's own size: compile-time offsets from one base per row
+      // (a row-major row is one run of vector loads)
+      auto load_exact = [&](auto colc) {
+        constexpr bool COL = decltype(colc)::value;
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const int q = tx + K * T;
+          const int qq = live && q < n ? q : 0;
+          const Real* lr = Ls + (COL ? qq : qq * N);
+          sfor<0, N>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            a[K][c] = lr[COL ? c * N : c];
+          });
+        });
+      };
+      if (col)
+        load_exact(std::true_type{});
+      else
+        load_exact(std::false_type{});
+    } else {
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        const int q = tx + K * T;
+        const bool qrow = live && q < n;
+        const int qq = qrow ? q : 0;
+        sfor<0, N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          a[K][c] = (q == c) ? Real(1) : Real(0);
+          if (qrow && c < n) a[K][c] = Ls[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
+        });
+      });
+    }
+  };
+  if constexpr (EARLY_LU) load_lu();
+
   // ---- the swap sequence to LDS (the identity past n and for groups past
   // the batch), then the source row of each position: walking the swaps
   // from the last to the first maps a position to the row it receives.
@@ -96,33 +147,19 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       src[K] = src[K] == k ? pk : (src[K] == pk ? k : src[K]);
     });
   });
+  if constexpr (!EARLY_LU) load_lu();
 
-  // ---- load: row q of L\U and row src(q) of B for each position q of the
-  // lane; past n the factors are the identity and B is zero.  Source rows
-  // are clamped into the matrix, so a malformed pivot cannot address
-  // outside it.
-  Real a[R][N];
-  Real y[R][NRHS];
   {
-    const Real* Ls = LU + sys_start(live ? sys : 0, ilv, (int64_t)n * n);
     const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
     auto src_row = [&](int K) { return src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]); };
-    if (n == N && nrhs == NRHS && ilv == 1) {
-      // the kernel's own size: compile-time offsets from one base per row
-      // (a row-major row is one run of vector loads)
-      auto load_exact = [&](auto colc) {
+    if (exact) {
+      auto load_b = [&](auto colc) {
         constexpr bool COL = decltype(colc)::value;
         sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
           const int q = tx + K * T;
-          const int qq = live && q < n ? q : 0;
           const int sr = src_row(K);
-          const Real* lr = Ls + (COL ? qq : qq * N);
           const Real* br = Bs + (COL ? sr : sr * NRHS);
-          sfor<0, N>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            a[K][c] = lr[COL ? c * N : c];
-          });
           sfor<0, NRHS>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             y[K][j] = q < N ? br[COL ? j * N : j] : Real(0);
@@ -130,21 +167,15 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         });
       };
       if (col)
-        load_exact(std::true_type{});
+        load_b(std::true_type{});
       else
-        load_exact(std::false_type{});
+        load_b(std::false_type{});
     } else {
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
         const bool qrow = live && q < n;
-        const int qq = qrow ? q : 0;
         const int sr = src_row(K);
-        sfor<0, N>([&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-          a[K][c] = (q == c) ? Real(1) : Real(0);
-          if (qrow && c < n) a[K][c] = Ls[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
-        });
         sfor<0, NRHS>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           y[K][j] = Real(0);
