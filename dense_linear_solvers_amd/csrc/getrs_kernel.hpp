@@ -48,7 +48,12 @@ struct GetrsShape {
   // n = 64 with 8, 1.8x at n = 16 with 4, 13% slower at n = 24 with 2)
   static constexpr bool CLASSES = NRHS >= 4;
   static constexpr int ELEMS = CLASSES ? (TRI + VEC - 1) / VEC * VEC : 0;
-  static constexpr int GROUP_BYTES = PIV_BYTES + ELEMS * (int)sizeof(Real);
+  // 16- and 64-lane groups load B unpermuted with L\U and permute it
+  // through LDS (the class area when there is one, else a staging area)
+  static constexpr bool EARLY = T >= 16;
+  static constexpr int STAGE =
+      (EARLY && !CLASSES) ? (N * NRHS * (int)sizeof(Real) + 15) / 16 * 16 : 0;
+  static constexpr int GROUP_BYTES = PIV_BYTES + ELEMS * (int)sizeof(Real) + STAGE;
   static constexpr int BLOCK_BYTES = kWavesPerBlock * G * GROUP_BYTES;
 };
 
@@ -75,19 +80,22 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   unsigned char* glds = lds_raw + (wave * G + g) * S::GROUP_BYTES;
   int32_t* pl = reinterpret_cast<int32_t*>(glds);
 
-  // ---- load, in two parts: row q of L\U for each position q of the lane
-  // (past n the identity), and row src(q) of B (past n zero) once the pivot
-  // walk below has named it.  Source rows are clamped into the matrix, so a
-  // malformed pivot cannot address outside it.  With 16- and 64-lane groups
-  // L\U is loaded before the walk, which it does not depend on, so its
-  // latency overlaps the walk (n = 32 float64: 0.444 -> 0.413 ms, n = 64:
-  // 1.43 -> 1.39 ms); with quads (four rows per lane) the rows would stay
-  // live through the walk and cost occupancy (n = 16 float32: 0.0265 ->
-  // 0.031 ms), so there they follow it.
-  constexpr bool EARLY_LU = T >= 16;
+  // ---- load: row q of L\U for each position q of the lane (past n the
+  // identity), and row src(q) of B (past n zero), src(q) being the row the
+  // pivot walk below brings to position q.  Source rows are clamped into
+  // the matrix, so a malformed pivot cannot address outside it.  With 16-
+  // and 64-lane groups both are loaded before the walk, which they do not
+  // depend on, so their latency overlaps it: B by original row, put in
+  // pivoted order through LDS afterwards (n = 32 float64: 0.444 -> 0.415 ms
+  // for the early L\U alone).  With quads (four rows per lane) the rows
+  // would stay live through the walk and cost occupancy (n = 16 float32:
+  // 0.0265 -> 0.031 ms), so there both follow it and B is read in pivoted
+  // order directly.
+  constexpr bool EARLY_LU = S::EARLY;
   Real a[R][N];
   Real y[R][NRHS];
   const bool exact = n == N && nrhs == NRHS && ilv == 1;
+  const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
   auto load_lu = [&]() {
     const Real* Ls = LU + sys_start(live ? sys : 0, ilv, (int64_t)n * n);
     if (exact) {
@@ -104,6 +112,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             constexpr int c = decltype(cc)::value;
             a[K][c] = lr[COL ? c * N : c];
           });
+          if constexpr (EARLY_LU) {   // row q of B, put in pivoted order later
+            const Real* br = Bs + (COL ? qq : qq * NRHS);
+            sfor<0, NRHS>([&](auto jc) {
+              constexpr int j = decltype(jc)::value;
+              y[K][j] = br[COL ? j * N : j];
+            });
+          }
         });
       };
       if (col)
@@ -121,6 +136,14 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           a[K][c] = (q == c) ? Real(1) : Real(0);
           if (qrow && c < n) a[K][c] = Ls[(col ? (int64_t)c * n + qq : (int64_t)qq * n + c) * ilv];
         });
+        if constexpr (EARLY_LU) {   // row q of B, put in pivoted order later
+          sfor<0, NRHS>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            y[K][j] = Real(0);
+            if (qrow && j < nrhs)
+              y[K][j] = Bs[(col ? (int64_t)j * n + qq : (int64_t)qq * nrhs + j) * ilv];
+          });
+        }
       });
     }
   };
@@ -149,9 +172,33 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   });
   if constexpr (!EARLY_LU) load_lu();
 
-  {
-    const Real* Bs = Bm + sys_start(live ? sys : 0, ilv, (int64_t)n * nrhs);
-    auto src_row = [&](int K) { return src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]); };
+  auto src_row = [&](int K) { return src[K] < 0 ? 0 : (src[K] >= n ? n - 1 : src[K]); };
+  if constexpr (EARLY_LU) {
+    // B by original row to LDS (after the swap sequence, which it follows
+    // in memory), then each position reads its source row
+    Real* stg = reinterpret_cast<Real*>(glds + S::PIV_BYTES);
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      if (q < n) {
+        sfor<0, NRHS>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          stg[q * NRHS + j] = y[K][j];
+        });
+      }
+    });
+    wave_sync_lds();
+    sfor<0, R>([&](auto Kc) {
+      constexpr int K = decltype(Kc)::value;
+      const int q = tx + K * T;
+      const Real* sr = stg + src_row(K) * NRHS;
+      sfor<0, NRHS>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        y[K][j] = (q < n) ? sr[j] : Real(0);
+      });
+    });
+    wave_sync_lds();   // read before the staging area is reused
+  } else {
     if (exact) {
       auto load_b = [&](auto colc) {
         constexpr bool COL = decltype(colc)::value;

@@ -148,7 +148,10 @@ constexpr int getrs_lds_bytes(int N, int NRHS, int T, bool is64) {
   const int utri = (N * (N + 1) / 2 + vec - 1) / vec * vec;
   const int tri = utri > N * NRHS ? utri : N * NRHS;
   const int elems = NRHS >= 4 ? (tri + vec - 1) / vec * vec : 0;
-  return kWavesPerBlock * (kWaveSize / T) * (piv + elems * es);
+  // 16- and 64-lane groups put B in pivoted order through LDS: the class
+  // area when there is one, else a staging area of N x NRHS
+  const int stage = (T >= 16 && NRHS < 4) ? (N * NRHS * es + 15) / 16 * 16 : 0;
+  return kWavesPerBlock * (kWaveSize / T) * (piv + elems * es + stage);
 }
 
 // LDS bytes of one block (one wave) of the Cholesky kernel: per group, the

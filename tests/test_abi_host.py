@@ -168,7 +168,8 @@ def test_plan_op_validation_and_shapes(lib):
                 vec = 16 // es
                 tri = max(-(-(N * (N + 1) // 2) // vec) * vec, N * R)
                 elems = -(-tri // vec) * vec if R >= 4 else 0
-                per_group = -(-(N * 4) // 16) * 16 + elems * es
+                stage = -(-(N * R * es) // 16) * 16 if (R < 4 and s["group_size"] >= 16) else 0
+                per_group = -(-(N * 4) // 16) * 16 + elems * es + stage
                 assert s["lds_bytes"] == s["systems_per_wave"] * per_group
                 assert s["systems_per_block"] * s["grid"] >= 1000
 
