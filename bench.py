@@ -224,12 +224,15 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
 
 
 def cpu_baseline(w, op: str = "gesv", min_seconds: float = 10.0,
-                 max_seconds: float = 30.0) -> dict:
-    """The CPU oracle, as it stands, on all cores of this host, over the
-    same inputs; repeated until at least ``min_seconds`` of work."""
+                 max_seconds: float = 30.0, threads: int = 0) -> dict:
+    """The CPU oracle, as it stands, on all cores of this host (or on
+    ``threads`` of them), over the same inputs; repeated until at least
+    ``min_seconds`` of work."""
     sys.path.insert(0, ROOT)
     import oracle
     cores = len(os.sched_getaffinity(0))
+    if threads > 0:
+        cores = min(cores, threads)
     A = np.ascontiguousarray(w.A)
     B = np.ascontiguousarray(w.B)
     n, nrhs, layout = w.n, w.nrhs, w.layout
@@ -290,6 +293,8 @@ def main():
                     help="store the batch with W systems interleaved element by element "
                          "(W = batch: structure of arrays); the *_ex calls")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU oracle baseline (default: every core of the process)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
                                                              "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -435,7 +440,7 @@ def main():
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, op)
+        result["cpu_baseline"] = cpu_baseline(w, op, threads=args.cpu_threads)
     print(json.dumps(result), flush=True)
 
 
