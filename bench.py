@@ -426,7 +426,9 @@ def main():
         "config": {"workload": w.name, "op": op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
                    **({"interleave": W} if W > 1 else {}),
                    "layout": "column-major" if w.layout == "col" else "row-major",
-                   "distribution": w.meta.get("recipe"), "seed": 0,
+                   "distribution": w.meta.get("recipe") + (
+                       " (redraw off here: no system was redrawn)"
+                       if w.meta.get("gap_filtered") is False else ""), "seed": 0,
                    **({"gap_filtered": False} if "gap_filtered" in w.meta else {}),
                    "group_size": plan["group_size"], "systems_per_wave": plan["systems_per_wave"]},
         "kernel_ms": kernel_ms,
