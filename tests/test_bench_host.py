@@ -1,7 +1,7 @@
 """bench.py's host-side pieces (CPU only): the algorithmic work per system
 against hand counts, the interleaving of its inputs against the element
 formula of the C interface, the source hash that keys the committed HBM
-counters, and the one-GPU guard."""
+counters, the one-GPU guard and the thread count of the oracle baseline."""
 from __future__ import annotations
 
 import os
@@ -89,3 +89,15 @@ def test_traffic_summary_round_trip(tmp_path):
         r = bench.read_traffic(f)
         assert os.path.basename(f) == f"{r['op']}_{r['workload']}_traffic.txt"
         assert float(r["hbm_bytes_per_launch"]) > 0
+
+
+def test_cpu_baseline_thread_count():
+    # the oracle leg reports the threads it ran on, capped at the process's cores
+    from dense_linear_solvers_amd import workloads
+    w = workloads.make("n8_f32_row", batch=256)
+    one = bench.cpu_baseline(w, "gesv", min_seconds=0.02, max_seconds=0.5, threads=1)
+    assert one["cores"] == 1 and one["value"] > 0 and one["kind"] == "oracle"
+    every = bench.cpu_baseline(w, "gesv", min_seconds=0.02, max_seconds=0.5)
+    assert every["cores"] == len(os.sched_getaffinity(0))
+    capped = bench.cpu_baseline(w, "gesv", min_seconds=0.02, max_seconds=0.5, threads=10**6)
+    assert capped["cores"] == every["cores"]
