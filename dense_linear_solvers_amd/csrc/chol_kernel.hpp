@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         sfor<js, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
           const Real l = K > js ? a[K][j] : (tx > jl ? a[K][j] : Real(0));
-          y[K][0] = __builtin_fma(-l, yb, y[K][0]);
+          y[K][0] = fma_r(-l, yb, y[K][0]);
         });
       });
     }
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           const Real yb = group_bcast<T, BL>(y[js][r]);
           sfor<js, R>([&](auto Kc) {
             constexpr int K = decltype(Kc)::value;
-            y[K][r] = __builtin_fma(-lm[K], yb, y[K][r]);
+            y[K][r] = fma_r(-lm[K], yb, y[K][r]);
           });
         }
       });
@@ -537,7 +537,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             yb = lane_fetch_any(yk, gb + kp * NJ + j0);
           sfor<km, QR>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
-            yv[m][jj] = __builtin_fma(-lik[m], yb, yv[m][jj]);
+            yv[m][jj] = fma_r(-lik[m], yb, yv[m][jj]);
           });
         });
       });
@@ -566,7 +566,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
             xb = lane_fetch_any(x, gb + kp * NJ + j0);
           sfor<0, km + 1>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
-            yv[m][jj] = __builtin_fma(-lkq[m], xb, yv[m][jj]);
+            yv[m][jj] = fma_r(-lkq[m], xb, yv[m][jj]);
           });
         });
       });

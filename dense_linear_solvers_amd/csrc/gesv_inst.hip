@@ -6,6 +6,8 @@
 #include "getrs_kernel.hpp"
 #include "chol_kernel.hpp"
 
+#include <tuple>
+
 #if !defined(TDLS_INST_SFX) || !defined(TDLS_INST_REAL) || !defined(TDLS_INST_N) || \
     !defined(TDLS_INST_NRHS)
 #error "gesv_inst.hip is compiled once per shape with the TDLS_INST_* macros defined"
@@ -15,6 +17,26 @@
 #define TDLS_LAUNCHER_NAME(sfx, N, NRHS) TDLS_LAUNCHER_NAME_(sfx, N, NRHS)
 
 namespace tdls {
+
+// Enqueue `kernel` and return the status of this launch alone.  The
+// arguments are converted to the kernel's parameter types and passed by
+// address (hipLaunchKernel), so the per-thread "last error" of the HIP
+// runtime is neither read nor cleared here: an earlier error of the caller
+// is left for the caller, and a failure of this launch is reported as this
+// launch's.
+template <typename... P, typename... Arg>
+static int launch_kernel(void (*kernel)(P...), unsigned grid, unsigned threads, int lds,
+                         hipStream_t stream, Arg... arg) {
+  static_assert(sizeof...(P) == sizeof...(Arg), "argument count of the kernel");
+  std::tuple<P...> vals(static_cast<P>(arg)...);
+  void* ptrs[sizeof...(P)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(threads),
+                              ptrs, (size_t)lds, stream);
+}
 
 template <typename Real, int N, int NRHS, int T, bool FACT>
 static int launch_panel(const LaunchPlan& p, const void* A, const void* B, void* X,
@@ -32,11 +54,10 @@ static int launch_panel(const LaunchPlan& p, const void* A, const void* B, void*
         hipFuncAttributeMaxDynamicSharedMemorySize, S::BLOCK_BYTES);
     if (allowed != hipSuccess) return (int)allowed;
   }
-  hipLaunchKernelGGL((gesv_panel_kernel<Real, N, NRHS, T, PB, FACT>), dim3((unsigned)p.grid),
-                     dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
-                     p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),
-                     static_cast<Real*>(X), piv, info, p.flags, p.interleave);
-  return (int)hipGetLastError();
+  return launch_kernel(&gesv_panel_kernel<Real, N, NRHS, T, PB, FACT>, (unsigned)p.grid,
+                       (unsigned)p.threads_per_block, S::BLOCK_BYTES, stream, p.layout, p.n,
+                       p.nrhs, p.batch, static_cast<const Real*>(A), static_cast<const Real*>(B),
+                       static_cast<Real*>(X), piv, info, p.flags, p.interleave);
 }
 
 template <typename Real, int N, int NRHS, int T>
@@ -46,11 +67,10 @@ static int launch_getrs(const LaunchPlan& p, const void* LU, const void* B, void
   static_assert(S::BLOCK_BYTES == getrs_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
                 "host and device LDS sizes disagree");
   if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((getrs_kernel<Real, N, NRHS, T>), dim3((unsigned)p.grid),
-                     dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
-                     p.batch, static_cast<const Real*>(LU), piv, static_cast<const Real*>(B),
-                     static_cast<Real*>(X), p.interleave);
-  return (int)hipGetLastError();
+  return launch_kernel(&getrs_kernel<Real, N, NRHS, T>, (unsigned)p.grid,
+                       (unsigned)p.threads_per_block, S::BLOCK_BYTES, stream, p.layout, p.n,
+                       p.nrhs, p.batch, static_cast<const Real*>(LU), piv,
+                       static_cast<const Real*>(B), static_cast<Real*>(X), p.interleave);
 }
 
 template <typename Real, int N, int NRHS, int T, bool FACT, bool SOLVE = false>
@@ -64,11 +84,10 @@ static int launch_chol(const LaunchPlan& p, const void* A, const void* B, void* 
                   "host and device LDS sizes disagree");
     static_assert(S::BLOCK_BYTES <= 65536, "Cholesky LDS stays within the default limit");
     if (p.lds_bytes != S::BLOCK_BYTES) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((chol_kernel<Real, N, NRHS, T, FACT, SOLVE>), dim3((unsigned)p.grid),
-                       dim3(p.threads_per_block), S::BLOCK_BYTES, stream, p.layout, p.n, p.nrhs,
-                       p.batch, (Real)p.shift, static_cast<const Real*>(A),
-                       static_cast<const Real*>(B), static_cast<Real*>(X), info, p.interleave);
-    return (int)hipGetLastError();
+    return launch_kernel(&chol_kernel<Real, N, NRHS, T, FACT, SOLVE>, (unsigned)p.grid,
+                         (unsigned)p.threads_per_block, S::BLOCK_BYTES, stream, p.layout, p.n,
+                         p.nrhs, p.batch, (Real)p.shift, static_cast<const Real*>(A),
+                         static_cast<const Real*>(B), static_cast<Real*>(X), info, p.interleave);
   }
 }
 

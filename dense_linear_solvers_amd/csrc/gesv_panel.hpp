@@ -56,6 +56,16 @@
 
 namespace tdls {
 
+// Fused multiply-add and magnitude in the working precision.  The plain
+// __builtin_fma / __builtin_fabs take and return double: on float operands
+// they would compute in double and round back, and a double fma rounded to
+// float is not always the float fma (the exact sum can round twice to the
+// other side of a float midpoint).  Every kernel uses these instead.
+__device__ __forceinline__ float fma_r(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_r(double a, double b, double c) { return __builtin_fma(a, b, c); }
+__device__ __forceinline__ float fabs_r(float v) { return __builtin_fabsf(v); }
+__device__ __forceinline__ double fabs_r(double v) { return __builtin_fabs(v); }
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void sfor(F&& f) {
   if constexpr (B < E) {
@@ -86,14 +96,12 @@ struct PanelShape {
   static constexpr int VEC = RealTraits<Real>::VEC;
   static constexpr int REC = N + NRHS;             // largest record: panel 0
   static constexpr int REC_STRIDE = (REC + VEC - 1) / VEC * VEC;
-  // Back substitution: first the right-hand sides by position (N x NRHS),
-  // then, over them, the upper-triangular store of U (row q holds columns
-  // q..N-1, rows packed one after another).
-  static constexpr int UTRI = N * (N + 1) / 2;
-  static constexpr int UTRI_PAD = (UTRI + VEC - 1) / VEC * VEC;   // keep 16-byte alignment
-  static constexpr int YAREA = N * NRHS;
-  static constexpr int BIG1 = B * REC_STRIDE > UTRI_PAD ? B * REC_STRIDE : UTRI_PAD;
-  static constexpr int GROUP_ELEMS = BIG1 > YAREA ? BIG1 : YAREA;
+  // U stays in registers for the back substitution (else: the right-hand
+  // sides by position, then over them the packed upper triangle of U, row q
+  // holding columns q..N-1); the group's LDS area, lu_group_elems
+  static constexpr bool REG_SOLVE = lu_solve_in_registers(NRHS, T);
+  static_assert(B == panel_width(N, NRHS, sizeof(Real) == 8), "panel width");
+  static constexpr int GROUP_ELEMS = lu_group_elems(N, NRHS, T, sizeof(Real) == 8);
   static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
   static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
 };
@@ -127,6 +135,28 @@ __device__ __forceinline__ uint32_t group_reduce(uint32_t v) {
         uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
         v = op(op(r0, r1), op(r2, r3));
       }
+    }
+  }
+  return v;
+}
+
+// Bitwise OR over the T lanes of a group (T < 64: DPP only, nothing goes
+// through the LDS crossbar).  With exactly one lane of each group holding a
+// non-zero value this hands that value to the whole group.
+template <int T>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+  static_assert(T < 64, "whole-wave groups use readlane");
+  if constexpr (T == 4) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true);  // xor 1
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, true);  // xor 2
+  } else {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, true);  // ror 8
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, true);  // ror 4
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, true);  // ror 2
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, true);  // ror 1
+    if constexpr (T == 32) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      v = (uint32_t)sw[0] | (uint32_t)sw[1];
     }
   }
   return v;
@@ -204,7 +234,7 @@ __device__ __forceinline__ void fnmac_bcast(double& acc, double u, double m) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, qp, 0xf, 0xf, true);
     const uint32_t hi =
         (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), qp, 0xf, 0xf, true);
-    acc = __builtin_fma(-m, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo), acc);
+    acc = fma_r(-m, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo), acc);
   }
 }
 template <int T, int L, bool NOP>
@@ -389,7 +419,7 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
         const Real xk = lane_fetch<T>(x, gbase + kl);
         sfor<0, ks + 1>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          yv[K][0] = __builtin_fma(-uk[K], xk, yv[K][0]);
+          yv[K][0] = fma_r(-uk[K], xk, yv[K][0]);
         });
       }
     });
@@ -441,7 +471,7 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
           xk = lane_fetch_any(x, src);
         sfor<0, km + 1>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
-          yv[m][jj] = __builtin_fma(-uk[m], xk, yv[m][jj]);
+          yv[m][jj] = fma_r(-uk[m], xk, yv[m][jj]);
         });
       });
     });
@@ -610,7 +640,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       const int q = tx + K * T;
       sfor<0, N>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
-        const Real v = (q < n && c < n) ? __builtin_fabs(a[K][c]) : Real(0);
+        const Real v = (q < n && c < n) ? fabs_r(a[K][c]) : Real(0);
         if constexpr (is64) {
           const uint32_t h = hi_word(v), l = lo_word(v);
           const bool gt = h > mh || (h == mh && l > ml);
@@ -807,9 +837,12 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           cpan[c] = take ? a[K][k + 1 + c] : cpan[c];
         });
       };
-      int wl;   // winning lane
+      int wl;       // winning lane
+      bool iswin;   // this lane holds its group's pivot row
       if (__builtin_expect(ntop == G, 1)) {
         sfor<K0 + 1, R>([&](auto Kc) { choose(Kc, tp[decltype(Kc)::value]); });
+        iswin = false;
+        sfor<K0, R>([&](auto Kc) { iswin |= tp[decltype(Kc)::value]; });
         if constexpr (T == 64) {
           wl = __builtin_ctzll(tmask);
         } else {
@@ -842,21 +875,52 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         }
         const uint32_t kmin = group_reduce<T, false>(top ? ck : 0xffffffffu);
         wl = (int)((kmin >> 5) & 63u);
+        iswin = lane == wl;
       }
-      const int p = (int)lane_fetch_u32<T>((uint32_t)cp, wl);   // winner's position
+      // The winner's position and pivot value reach its group.  The group
+      // maximum mh already holds the pivot's magnitude bits (of the high
+      // word in float64); the winner adds its sign and position, and in
+      // float64 its low word, by a DPP OR over the group of values only it
+      // holds (nothing through the LDS crossbar); whole-wave groups read
+      // them from the winning lane.
+      int p;          // winner's position
+      Real dpiv;      // the pivot
+      if constexpr (T == 64) {
+        p = (int)lane_fetch_u32<T>((uint32_t)cp, wl);
+        if constexpr (is64)
+          dpiv = __builtin_bit_cast(double, ((uint64_t)lane_fetch_u32<T>(ch, wl) << 32) |
+                                                lane_fetch_u32<T>(cl, wl));
+        else
+          dpiv = __builtin_bit_cast(float, lane_fetch_u32<T>(ch, wl));
+      } else {
+        const uint32_t sp = group_or<T>(iswin ? ((ch & 0x80000000u) | (uint32_t)cp) : 0u);
+        p = (int)(sp & 0x7fffffffu);
+        const uint32_t dh = (mh & 0x7fffffffu) | (sp & 0x80000000u);
+        if constexpr (is64)
+          dpiv = __builtin_bit_cast(double, ((uint64_t)dh << 32) | group_or<T>(iswin ? cl : 0u));
+        else
+          dpiv = __builtin_bit_cast(float, dh);
+      }
+      // the winner's entries right of k inside the panel, the same way (the
+      // LDS crossbar is the busier resource: measured, DPP ORs beat lane
+      // fetches here even in 16-lane groups)
       Real upan[PC > 0 ? PC : 1];                          // pivot row, right of k
       sfor<0, PC>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
-        upan[c] = lane_fetch<T>(cpan[c], wl);
+        if constexpr (T == 64) {
+          upan[c] = lane_fetch<T>(cpan[c], wl);
+        } else if constexpr (is64) {
+          const uint64_t b = __builtin_bit_cast(uint64_t, cpan[c]);
+          const uint32_t h = group_or<T>(iswin ? (uint32_t)(b >> 32) : 0u);
+          const uint32_t l = group_or<T>(iswin ? (uint32_t)b : 0u);
+          upan[c] = __builtin_bit_cast(double, ((uint64_t)h << 32) | l);
+        } else {
+          upan[c] = __builtin_bit_cast(
+              float, group_or<T>(iswin ? __builtin_bit_cast(uint32_t, cpan[c]) : 0u));
+        }
       });
-      Real dpiv;
-      if constexpr (is64)
-        dpiv = __builtin_bit_cast(double, ((uint64_t)lane_fetch_u32<T>(ch, wl) << 32) |
-                                              lane_fetch_u32<T>(cl, wl));
-      else
-        dpiv = __builtin_bit_cast(float, lane_fetch_u32<T>(ch, wl));
       const bool zero_pivot = dpiv == Real(0);
-      pz = __builtin_fma(dpiv, Real(0), pz);
+      pz = fma_r(dpiv, Real(0), pz);
       asm volatile("" : "+v"(pz));   // in place, not sunk to the end
       if (zero_pivot && status == 0) status = k + 1;
       // settle the status here: left to the end, the per-step zero flags of
@@ -891,7 +955,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         constexpr int c = decltype(cc)::value;
         sfor<K0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          a[K][k + 1 + c] = __builtin_fma(-lm[i][K], upan[c], a[K][k + 1 + c]);
+          a[K][k + 1 + c] = fma_r(-lm[i][K], upan[c], a[K][k + 1 + c]);
         });
       });
     });
@@ -951,7 +1015,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           const Real lmj = rec[j * S::REC_STRIDE + W + m];
           sfor<0, NU>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            u[j][r] = __builtin_fma(-lmj, u[m][r], u[j][r]);
+            u[j][r] = fma_r(-lmj, u[m][r], u[j][r]);
           });
         });
       });
@@ -1060,7 +1124,80 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     // from its position on) by position
     int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
     wave_sync_lds();  // the last records have been read
-    const bool xbad = upper_solve_store<Real, N, NRHS, T>(
+    bool xbad;
+    if constexpr (S::REG_SOLVE) {
+      // ---- back substitution from registers (one right-hand side, the
+      // group a DPP domain).  Every slot but the last already holds its
+      // positions in order (slot K, lane tx: position K*T + tx) since the
+      // last slot boundary; the rows of the last slot, permuted among
+      // themselves by the steps since, go through LDS and come back in
+      // position order (their U part, columns from the slot's first
+      // position on, and their right-hand side).
+      static_assert(R == 1 || COMPACT, "slots below the last are in position order");
+      constexpr int KL = R - 1;
+      constexpr int Q0 = KL * T;                 // first position of the last slot
+      constexpr int NS2 = N - Q0;                // its rows
+      constexpr int E2 = N - Q0 + NRHS;          // entries moved per row
+      constexpr int CM2 = S::GROUP_ELEMS / NS2 / VEC * VEC;
+      constexpr int RS2 = ((CM2 * (int)sizeof(Real) / 4) % 32 == 0 && CM2 > VEC) ? CM2 - VEC : CM2;
+      static_assert(RS2 >= VEC && NS2 * RS2 <= S::GROUP_ELEMS, "staging fits the group area");
+      constexpr int NCH2 = (E2 + RS2 - 1) / RS2;
+      auto ent2 = [&](auto ec) -> Real& {
+        constexpr int e = decltype(ec)::value;
+        if constexpr (e < N - Q0) return a[KL][Q0 + e];
+        else return y[KL][e - (N - Q0)];
+      };
+      sfor<0, NCH2>([&](auto hc) {
+        constexpr int e0 = decltype(hc)::value * RS2;
+        constexpr int e1 = (e0 + RS2) < E2 ? (e0 + RS2) : E2;
+        const int p = lab[KL];
+        if (p >= Q0) {
+          Real* dst = rec + (p - Q0) * RS2 - e0;   // entry e at dst[e]
+          sfor<e0, e1>([&](auto ec) { dst[decltype(ec)::value] = ent2(ec); });
+        }
+        wave_sync_lds();
+        if (Q0 + tx < N) {
+          const Real* src = rec + tx * RS2 - e0;
+          sfor<e0, e1>([&](auto ec) { ent2(ec) = src[decltype(ec)::value]; });
+        }
+        wave_sync_lds();
+      });
+      // U x = y: x_k = y_k / U(k,k) by IEEE division on lane k % T (slot
+      // k / T) for k = n-1 .. 0, removed from the rows above by DPP inside
+      // the fused multiply-add (the order of the TDLS page's Detailed
+      // Description, the solution entry kept by its owner)
+      Real xr[R];
+      sfor<0, R>([&](auto Kc) { xr[decltype(Kc)::value] = Real(0); });
+      sfor<0, N>([&](auto ic) {
+        constexpr int k = N - 1 - decltype(ic)::value;
+        constexpr int kl = k % T;
+        constexpr int ks = k / T;
+        constexpr int SLK = kl % SL;
+        const Real x = y[ks][0] / a[ks][k];   // meaningful on lane kl
+        xr[ks] = tx == kl ? x : xr[ks];
+        asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
+        sfor<0, ks + 1>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          fnmac_bcast<T, SLK, K == 0>(y[K][0], x, a[K][k]);
+        });
+      });
+      bool bad = false;
+      sfor<0, R>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        bad |= (tx + K * T < n) & not_finite(xr[K]);
+      });
+      xbad = group_any<T>(bad, gbase);
+      if (live) {
+        const bool zero = status != 0 || nf || xbad;
+        Real* Xs = X + sys_start(sys, ilv, (int64_t)n * nrhs);
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          const int q = tx + K * T;
+          if (q < n) Xs[q * ilv] = zero ? Real(0) : xr[K];   // one column: same address in both layouts
+        });
+      }
+    } else
+    xbad = upper_solve_store<Real, N, NRHS, T>(
         rec, tx, gbase, live, status != 0 || nf, live ? sys : 0, n, nrhs, col, ilv, X,
         [&](Real* yt) {
           sfor<0, R>([&](auto Kc) {

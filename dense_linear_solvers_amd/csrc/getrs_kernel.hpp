@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           yb = lane_fetch_any(yv[km][jj], gbase + kp * NJ + j0);
         sfor<km, QR>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
-          yv[m][jj] = __builtin_fma(-lik[m], yb, yv[m][jj]);
+          yv[m][jj] = fma_r(-lik[m], yb, yv[m][jj]);
         });
       });
     });
@@ -366,9 +366,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         const Real yk = lane_fetch<T>(y[ks][j], gbase + kl);
         sfor<ks + 1, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          y[K][j] = __builtin_fma(-a[K][k], yk, y[K][j]);
+          y[K][j] = fma_r(-a[K][k], yk, y[K][j]);
         });
-        y[ks][j] = __builtin_fma(-mk, yk, y[ks][j]);
+        y[ks][j] = fma_r(-mk, yk, y[ks][j]);
       }
     });
   });
@@ -400,9 +400,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         const Real xk = lane_fetch<T>(x, gbase + kl);
         sfor<0, ks>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
-          y[K][j] = __builtin_fma(-a[K][k], xk, y[K][j]);
+          y[K][j] = fma_r(-a[K][k], xk, y[K][j]);
         });
-        y[ks][j] = __builtin_fma(-mk, xk, y[ks][j]);
+        y[ks][j] = fma_r(-mk, xk, y[ks][j]);
       }
     });
   });

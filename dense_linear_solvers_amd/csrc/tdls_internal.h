@@ -122,19 +122,45 @@ constexpr int panel_width(int N, [[maybe_unused]] int NRHS, [[maybe_unused]] boo
   return N < 4 ? N : 4;
 }
 
-// LDS bytes of one block (one wave): per group, the largest of B records of
-// N + NRHS entries (rounded up to 16 bytes), the N x NRHS right-hand sides
-// by position and the packed upper-triangular store of U used by the back
-// substitution (the last two occupy the same area one after the other).
-constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
+// The LU solve keeps U in registers for the back substitution when one
+// right-hand side is broadcast inside a DPP domain (quads, 16-lane rows):
+// after a last compaction every slot holds its positions in order, so x_k
+// reaches the rows above from a fixed lane.  Otherwise U goes to a packed
+// triangle in LDS (several right-hand sides split over column classes;
+// whole-wave groups).
+constexpr bool lu_solve_in_registers(int NRHS, int T) { return NRHS == 1 && (T == 4 || T == 16); }
+
+// LDS a wave of the LU kernels may take so that twelve waves (three per
+// SIMD) fit the 160 KiB of a CU.
+constexpr int kLuLdsPerWave = 13312;
+
+// LDS elements of one group of the LU kernels: the B pivot-row records of
+// N + NRHS entries (rounded up to 16 bytes) and, where U stays in
+// registers, a staging area for putting rows back in position order (the
+// whole tile when it fits kLuLdsPerWave, else chunks of it); otherwise the
+// N x NRHS right-hand sides by position and the packed upper triangle of U
+// of the back substitution (the last two occupy the same area one after the
+// other).
+constexpr int lu_group_elems(int N, int NRHS, int T, bool is64) {
   const int es = is64 ? 8 : 4;
   const int vec = 16 / es;
   const int stride = (N + NRHS + vec - 1) / vec * vec;
   const int B = panel_width(N, NRHS, is64);
+  const int rec = B * stride;
+  if (lu_solve_in_registers(NRHS, T)) {
+    const int budget = kLuLdsPerWave / (kWaveSize / T) / es / vec * vec;
+    const int tile = (N * (N + NRHS) + vec - 1) / vec * vec;
+    const int stage = tile < budget ? tile : budget;
+    return rec > stage ? rec : stage;
+  }
   const int utri = (N * (N + 1) / 2 + vec - 1) / vec * vec;
-  const int big1 = B * stride > utri ? B * stride : utri;
-  const int group = big1 > N * NRHS ? big1 : N * NRHS;
-  return kWavesPerBlock * (kWaveSize / T) * group * es;
+  const int big1 = rec > utri ? rec : utri;
+  return big1 > N * NRHS ? big1 : N * NRHS;
+}
+
+// LDS bytes of one block (one wave) of the LU kernels (gesv, getrf).
+constexpr int gesv_lds_bytes(int N, int NRHS, int T, bool is64) {
+  return kWavesPerBlock * (kWaveSize / T) * lu_group_elems(N, NRHS, T, is64) * (is64 ? 8 : 4);
 }
 
 // LDS bytes of one block (one wave) of the getrs kernel: per group, the
