@@ -299,6 +299,30 @@ def _check_square(torch, A, name):
         raise ValueError(f"{name} must be [batch, n, n]")
 
 
+def _check_out(torch, t, name, dtype, device, shape):
+    """An ``out`` tensor must be exactly what the call would allocate: the
+    library sees raw pointers only, so a wrong size, type or device would be
+    written past or to the wrong memory.  Raises before any library call."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"out {name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"out {name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"out {name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"out {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"out {name} must be contiguous")
+
+
+def _unpack_out(out, names):
+    if len(names) == 1:
+        return (out,)
+    if not isinstance(out, (tuple, list)) or len(out) != len(names):
+        raise TypeError(f"out must be a tuple ({', '.join(names)})")
+    return tuple(out)
+
+
 def _interleaved_dims(A, B, layout: str, interleave: int, batch):
     """Problem sizes of interleaved operands: A [blocks, n, n, W] and B
     [blocks, n, nrhs, W] ("row") or [blocks, nrhs, n, W] ("col"), system s
@@ -382,7 +406,10 @@ def gesv_batched(A, B, layout: str = "row", out=None, stream=None, scale: bool =
         piv = torch.empty(_piv_shape(A, n, interleave), dtype=torch.int32, device=A.device)
         info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
-        X, piv, info = out
+        X, piv, info = _unpack_out(out, ("X", "piv", "info"))
+        _check_out(torch, X, "X", B.dtype, B.device, B.shape)
+        _check_out(torch, piv, "piv", torch.int32, A.device, _piv_shape(A, n, interleave))
+        _check_out(torch, info, "info", torch.int32, A.device, (nb,))
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):
@@ -420,7 +447,10 @@ def getrf_batched(A, layout: str = "row", out=None, stream=None, scale: bool = F
         piv = torch.empty(_piv_shape(A, n, interleave), dtype=torch.int32, device=A.device)
         info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
-        LU, piv, info = out
+        LU, piv, info = _unpack_out(out, ("LU", "piv", "info"))
+        _check_out(torch, LU, "LU", A.dtype, A.device, A.shape)
+        _check_out(torch, piv, "piv", torch.int32, A.device, _piv_shape(A, n, interleave))
+        _check_out(torch, info, "info", torch.int32, A.device, (nb,))
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):
@@ -453,6 +483,8 @@ def getrs_batched(LU, piv, B, layout: str = "row", out=None, stream=None, interl
         raise ValueError("piv must be a contiguous int32 tensor on LU's device, shaped as "
                          "getrf_batched returns it")
     X = torch.empty_like(B) if out is None else out
+    if out is not None:
+        _check_out(torch, X, "X", B.dtype, B.device, B.shape)
     s = stream if stream is not None else torch.cuda.current_stream(LU.device)
     dt = _dtype_code(torch, LU)
     with torch.cuda.device(LU.device):
@@ -487,7 +519,9 @@ def potrf_batched(A, layout: str = "row", shift: float = 0.0, out=None, stream=N
         L = torch.empty_like(A)
         info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
-        L, info = out
+        L, info = _unpack_out(out, ("L", "info"))
+        _check_out(torch, L, "L", A.dtype, A.device, A.shape)
+        _check_out(torch, info, "info", torch.int32, A.device, (nb,))
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):
@@ -515,6 +549,8 @@ def potrs_batched(L, B, layout: str = "row", out=None, stream=None, interleave: 
     _check_pair(torch, L, B, "L", "B")
     nb, n, nrhs = _dims(L, B, layout, interleave, batch)
     X = torch.empty_like(B) if out is None else out
+    if out is not None:
+        _check_out(torch, X, "X", B.dtype, B.device, B.shape)
     s = stream if stream is not None else torch.cuda.current_stream(L.device)
     dt = _dtype_code(torch, L)
     with torch.cuda.device(L.device):
@@ -542,7 +578,9 @@ def posv_batched(A, B, layout: str = "row", shift: float = 0.0, out=None, stream
         X = torch.empty_like(B)
         info = torch.empty((nb,), dtype=torch.int32, device=A.device)
     else:
-        X, info = out
+        X, info = _unpack_out(out, ("X", "info"))
+        _check_out(torch, X, "X", B.dtype, B.device, B.shape)
+        _check_out(torch, info, "info", torch.int32, A.device, (nb,))
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     dt = _dtype_code(torch, A)
     with torch.cuda.device(A.device):

@@ -139,6 +139,14 @@ int tdls_gesv_batched(tdls_dtype dtype, tdls_layout layout, int n, int nrhs, int
  * (host only: touches no device).  Validates the same scalar arguments
  * (codes -1 .. -5); returns -6 when out is NULL.
  *
+ * The launch plan is a host-side object that can be checked without a GPU,
+ * as the ruSOLVER page's section on building and verifying runs its
+ * launch-plan tests on the host before any device suite ("ruSOLVER：小矩阵
+ * kernel 优化（实验性）", 编译和验证).  The plan holds the group size T
+ * (lanes per system), rows per lane, systems per wave and per block, the
+ * grid and the LDS bytes of the one kernel the solve enqueues; `out` is
+ * caller-owned host memory, written only on success.
+ *
  * The environment variable TDLS_GROUP_SIZE, when set to a group size built
  * for the shape, overrides the planner's choice (used by the tests that
  * check results do not depend on it); an unbuilt value yields

@@ -359,3 +359,30 @@ def test_group_size_choice_per_op(lib):
             assert tdls.plan_op(op, "f64", "row", n, 1, big)["group_size"] == 4
         assert tdls.plan_gesv("f32", "row", n, 4, big)["group_size"] == 4
     assert tdls.plan_gesv("f64", "row", 8, 1, big)["group_size"] == 4
+
+
+def test_out_tensors_are_checked_before_any_call():
+    """``out=`` tensors must be exactly what the call would allocate (the C
+    layer sees raw pointers only); a mismatch raises before the library is
+    called.  Checked on CPU tensors against a CPU device."""
+    import torch
+    from dense_linear_solvers_amd import _binding as b
+    dev = torch.device("cpu")
+    good = torch.empty((4, 16, 2), dtype=torch.float64)
+    b._check_out(torch, good, "X", torch.float64, dev, (4, 16, 2))
+    with pytest.raises(TypeError):
+        b._check_out(torch, good.float(), "X", torch.float64, dev, (4, 16, 2))
+    with pytest.raises(ValueError):
+        b._check_out(torch, good[:3], "X", torch.float64, dev, (4, 16, 2))
+    with pytest.raises(ValueError):
+        b._check_out(torch, good.transpose(1, 2), "X", torch.float64, dev, (4, 2, 16))
+    with pytest.raises(ValueError):
+        b._check_out(torch, good, "X", torch.float64, torch.device("meta"), (4, 16, 2))
+    with pytest.raises(TypeError):
+        b._check_out(torch, good.numpy(), "X", torch.float64, dev, (4, 16, 2))
+    piv = torch.empty((4, 16), dtype=torch.int64)
+    with pytest.raises(TypeError):
+        b._check_out(torch, piv, "piv", torch.int32, dev, (4, 16))
+    with pytest.raises(TypeError):
+        b._unpack_out((good, piv), ("X", "piv", "info"))
+    assert b._unpack_out(good, ("X",)) == (good,)
