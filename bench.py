@@ -6,12 +6,20 @@ row exchange, elimination with the forward substitution folded in, back
 substitution and store, all in one kernel launch.  The default workload is
 n = 32, nrhs = 1, batch = 262144, float64, column-major, A and B iid N(0, 1)
 (the recipe ``n32_f64_col``; with seed 0 no system needs a pivot-gap redraw,
-which the test suite checks), inputs resident in HBM before timing starts.
+which tests/test_workloads.py checks over the whole batch), inputs resident
+in HBM before timing starts.
 
-Prints one JSON line.  ``value`` is systems solved per second; the roofline
-object prices the kernel's algorithmic HBM bytes per launch against 8 TB/s;
+Prints one JSON line.  ``value`` is systems solved per second over the
+timed steps (wall clock, launches back to back); the roofline object
+prices the kernel's algorithmic HBM bytes per launch against 8 TB/s, over
+the mean of per-launch HIP-event times on the launch stream (median, min
+and max are reported beside it); ``issue_floor`` is the VALU issue floor
+from the committed SQ counters (when they match the sources);
 ``cpu_baseline`` is the plain CPU oracle timed on this host's cores on the
-same inputs.
+same inputs.  Working sets below 512 MiB rotate over several buffer sets so
+that no launch is served from the 256 MB Infinity Cache.  After timing,
+``api_wall_ms`` samples synchronous calls (allocation, submission,
+execution and the wait), the ruSOLVER page's own measure.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME]
                   [--op gesv|getrf|getrs|potrf|potrs|posv] [--interleave W] [--no-cpu]
@@ -19,6 +27,7 @@ same inputs.
                                         # scaling the HBM byte counters
   python bench.py [--workload NAME] [--op OP] --summarize-counters \
                   FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+  python bench.py [--workload NAME] [--op OP] --summarize-sq PMC_DIR [PMC_DIR ...]
 """
 from __future__ import annotations
 
@@ -37,6 +46,9 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 FP64_VECTOR_PEAK_TFLOPS = 78.6   # MI355X, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 METRIC = "systems/sec + achieved HBM GB/s, batched LUPP gesv n=32 fp32/fp64"
+ROTATE_BELOW = 512 << 20         # working sets below this rotate buffer sets (MALL is 256 MB)
+SIMDS = 1024                     # MI355X: 256 CUs x 4 SIMDs
+CLOCK_GHZ = 2.4                  # MI355X peak engine clock, published
 DEFAULT_WORKLOAD = "n32_f64_col"
 
 
@@ -192,6 +204,154 @@ def summarize_counters(workload: str, op: str, fetch_dir: str, write_dir: str,
     return d
 
 
+def sq_path(workload: str, op: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{op}_{workload}_sq_counters.txt")
+
+
+def summarize_sq(workload: str, op: str, dirs: list) -> dict:
+    """Per-wave SQ counters of the solver kernel from rocprofv3 --pmc runs
+    (one directory per pass): each counter's median over dispatches of its
+    per-dispatch total, divided by the waves of a launch (grid threads / 64).
+    Counters named *CYCLES* or SQ_ACTIVE_INST_* / SQ_WAIT_* count quad-cycles
+    (4 clock cycles), except SQ_BUSY_CYCLES and SQ_LDS_* (clock cycles), as
+    rocprofv3's counter list states."""
+    import csv
+    import glob
+    kern = KERNEL_OF_OP[op]
+    per = {}          # counter -> list of per-dispatch totals
+    waves = vgpr = None
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            rows = {}
+            with open(f, encoding="utf-8") as fh:
+                for r in csv.DictReader(fh):
+                    if not r["Kernel_Name"].startswith(kern):
+                        continue
+                    rows.setdefault((r["Dispatch_Id"], r["Counter_Name"]), 0.0)
+                    rows[(r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
+                    waves = int(r["Grid_Size"]) // 64
+                    vgpr = int(r["VGPR_Count"]) + int(r.get("Accum_VGPR_Count") or 0)
+            for (_, c), v in rows.items():
+                per.setdefault(c, []).append(v)
+    if not per:
+        raise SystemExit(f"no counters for {kern} under {dirs}")
+    d = {"workload": workload, "op": op, "kernel": kern,
+         "kernel_source_hash": kernel_source_hash(), "waves_per_launch": waves,
+         "vgprs": vgpr}
+    for c in sorted(per):
+        d[f"{c}_per_wave"] = float(np.median(per[c])) / waves
+    q = d.get("SQ_ACTIVE_INST_VALU_per_wave")
+    if q is not None:
+        d["valu_floor_ms"] = waves * q * 4 / SIMDS / (CLOCK_GHZ * 1e6)
+    out = sq_path(workload, op)
+    head = [f"# SQ counters of {kern} ({op}) on {workload}, per wave (median over dispatches)",
+            TRAFFIC_MARKER]
+    if os.path.exists(out):
+        with open(out, encoding="utf-8") as fh:
+            old = fh.read().splitlines()
+        if TRAFFIC_MARKER in old:
+            head = old[:old.index(TRAFFIC_MARKER) + 1]
+    with open(out, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(head + traffic_lines(d)) + "\n")
+    return d
+
+
+def stats_path(workload: str, op: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{op}_{workload}_kernel_stats.txt")
+
+
+def summarize_trace(workload: str, op: str, trace_dir: str, bench_out: str, command: str) -> dict:
+    """profiles/<op>_<workload>_kernel_stats.txt from a rocprofv3
+    --kernel-trace --stats run of bench.py: the stats table, the solver
+    kernel's average launch time, and the bench line the same run printed
+    (its per-launch HIP-event times), so the two can be compared."""
+    import csv
+    import glob
+    kern = KERNEL_OF_OP[op]
+    files = glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    with open(files[0], encoding="utf-8") as fh:
+        text = fh.read()
+    rows = list(csv.DictReader(text.splitlines()))
+    mine = [r for r in rows if r["Name"].startswith(kern)]
+    if not mine:
+        raise SystemExit(f"no {kern} row in {files[0]}")
+    r = mine[0]
+    avg_ms = float(r["AverageNs"]) * 1e-6
+    line = None
+    with open(bench_out, encoding="utf-8") as fh:
+        for ln in fh:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    d = {"workload": workload, "op": op, "kernel": kern,
+         "kernel_source_hash": kernel_source_hash(), "calls": int(r["Calls"]),
+         "trace_avg_ms": avg_ms, "trace_min_ms": float(r["MinNs"]) * 1e-6,
+         "trace_max_ms": float(r["MaxNs"]) * 1e-6}
+    head = [f"# rocprofv3 kernel statistics: {op} on {workload}",
+            "# command (repository root, one MI355X):", f"#   {command}", "#"]
+    for ln in text.strip().splitlines():
+        head.append("# " + ln)
+    if line is not None:
+        kl = line["kernel_ms_per_launch"]
+        d.update({"bench_kernel_ms_mean": kl["mean"], "bench_kernel_ms_median": kl["median"],
+                  "bench_kernel_ms_min": kl["min"], "bench_kernel_ms_max": kl["max"],
+                  "bench_ms_per_step": line["ms_per_step"],
+                  "trace_vs_bench_mean": avg_ms / kl["mean"] - 1.0})
+        head += ["#", f"# {kern}: trace average {avg_ms:.4f} ms over {r['Calls']} dispatches "
+                 f"(min {d['trace_min_ms']:.4f}, max {d['trace_max_ms']:.4f}); the same run's "
+                 f"bench line: per-launch HIP events mean {kl['mean']:.4f} ms, median "
+                 f"{kl['median']:.4f}, min {kl['min']:.4f}, max {kl['max']:.4f}; ms_per_step "
+                 f"{line['ms_per_step']:.4f} (trace average {100 * d['trace_vs_bench_mean']:+.1f}% "
+                 "from the event mean)"]
+    head.append(TRAFFIC_MARKER)
+    with open(stats_path(workload, op), "w", encoding="utf-8") as fh:
+        fh.write("\n".join(head + traffic_lines(d)) + "\n")
+    return d
+
+
+def issue_floor(workload: str, op: str):
+    """VALU issue floor of one launch from the committed SQ summary, when it
+    was taken on the current kernel sources and at this batch: every wave's
+    VALU-active quad-cycles, 4 cycles each, spread over the 1024 SIMDs at the
+    2.4 GHz peak clock.  The recipe's own batch only."""
+    path = sq_path(workload, op)
+    if not os.path.exists(path):
+        return None
+    d = read_traffic(path)
+    if d.get("kernel_source_hash") != kernel_source_hash() or "valu_floor_ms" not in d:
+        return None
+    return {"valu_floor_ms": float(d["valu_floor_ms"]),
+            "valu_active_quad_cycles_per_wave": float(d["SQ_ACTIVE_INST_VALU_per_wave"]),
+            "waves_per_launch": int(d["waves_per_launch"]), "vgprs": int(d["vgprs"]),
+            "source": os.path.relpath(path, ROOT)}
+
+
+def run_info() -> dict:
+    """Device, software and source identity of a measurement (the ruSOLVER
+    page records configuration, device and source with every timing)."""
+    import platform
+    import torch
+    info = {"device": torch.cuda.get_device_name(0),
+            "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": platform.processor() or None,
+            "kernel_source_hash": kernel_source_hash()}
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["host_cpu"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    bi = os.path.join(ROOT, "dense_linear_solvers_amd", "_build", "build_info.json")
+    if os.path.exists(bi):
+        with open(bi, encoding="utf-8") as fh:
+            info["library_build"] = json.load(fh)
+    return info
+
+
 def interleave(x: np.ndarray, W: int) -> np.ndarray:
     """[batch, ...] -> [blocks, ..., W]: element e of system s at
     (s // W) W E + s % W + e W (the last block padded with zeros)."""
@@ -293,6 +453,16 @@ def main():
                     help="store the batch with W systems interleaved element by element "
                          "(W = batch: structure of arrays); the *_ex calls")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="one buffer set even when the working set is below 512 MiB")
+    ap.add_argument("--api-samples", type=int, default=10,
+                    help="synchronous API wall-clock samples after the timed region")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "BENCH_OUT", "COMMAND"),
+                    help="write profiles/<op>_<workload>_kernel_stats.txt from a rocprofv3 "
+                         "--kernel-trace --stats directory and the bench line of the same run")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/<op>_<workload>_sq_counters.txt from rocprofv3 --pmc "
+                         "output directories of SQ counters (no GPU needed)")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the CPU oracle baseline (default: every core of the process)")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -301,6 +471,12 @@ def main():
                     help="write the data lines of profiles/<op>_<workload>_traffic.txt from rocprofv3 --pmc "
                          "output directories (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.workload, args.op, *args.summarize_trace), indent=1))
+        return
+    if args.summarize_sq:
+        print(json.dumps(summarize_sq(args.workload, args.op, args.summarize_sq), indent=1))
+        return
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.workload, args.op, *args.summarize_counters),
                          indent=1))
@@ -332,51 +508,91 @@ def main():
     if W > w.batch:
         raise SystemExit("--interleave must not exceed the batch")
     ex = {"interleave": W, "batch": w.batch} if W > 1 else {}
-    A = torch.from_numpy(interleave(w.A, W) if W > 1 else w.A).to(dev)
-    B = torch.from_numpy(interleave(w.B, W) if W > 1 else w.B).to(dev)
-    X = torch.empty_like(B)
-    piv = torch.empty((A.shape[0], w.n, W) if W > 1 else (w.batch, w.n), dtype=torch.int32,
-                      device=dev)
-    info = torch.empty((w.batch,), dtype=torch.int32, device=dev)
-    out = (X, piv, info)
+    A_host = interleave(w.A, W) if W > 1 else w.A
+    B_host = interleave(w.B, W) if W > 1 else w.B
     stream = torch.cuda.current_stream(dev)
     op = args.op
     plan = tdls.plan_op(op, w.dtype, w.layout, w.n, w.nrhs, w.batch)
-    if op == "gesv":
-        step = lambda: tdls.gesv_batched(A, B, w.layout, out=out, **ex)
-    elif op == "getrf":
-        LU = torch.empty_like(A)
-        step = lambda: tdls.getrf_batched(A, w.layout, out=(LU, piv, info), **ex)
-    elif op == "getrs":
-        LU = torch.empty_like(A)
-        tdls.getrf_batched(A, w.layout, out=(LU, piv, info), **ex)     # factors, untimed
-        step = lambda: tdls.getrs_batched(LU, piv, B, w.layout, out=X, **ex)
-    elif op == "potrf":
-        Lc = torch.empty_like(A)
-        step = lambda: tdls.potrf_batched(A, w.layout, out=(Lc, info), **ex)
-    elif op == "potrs":
-        Lc = torch.empty_like(A)
-        tdls.potrf_batched(A, w.layout, out=(Lc, info), **ex)     # factors, untimed
-        step = lambda: tdls.potrs_batched(Lc, B, w.layout, out=X, **ex)
-    else:
-        step = lambda: tdls.posv_batched(A, B, w.layout, out=(X, info), **ex)
 
-    for _ in range(args.warmup):
-        step()
+    def make_set():
+        """Device buffers of one step: inputs (factors made here, untimed,
+        for getrs / potrs) and outputs."""
+        d = {"A": torch.from_numpy(A_host).to(dev), "B": torch.from_numpy(B_host).to(dev)}
+        d["X"] = torch.empty_like(d["B"])
+        d["piv"] = torch.empty((d["A"].shape[0], w.n, W) if W > 1 else (w.batch, w.n),
+                               dtype=torch.int32, device=dev)
+        d["info"] = torch.empty((w.batch,), dtype=torch.int32, device=dev)
+        if op in ("getrf", "getrs"):
+            d["LU"] = torch.empty_like(d["A"])
+        if op == "getrs":
+            tdls.getrf_batched(d["A"], w.layout, out=(d["LU"], d["piv"], d["info"]), **ex)
+        if op in ("potrf", "potrs"):
+            d["L"] = torch.empty_like(d["A"])
+        if op == "potrs":
+            tdls.potrf_batched(d["A"], w.layout, out=(d["L"], d["info"]), **ex)
+        return d
+
+    def run(d):
+        if op == "gesv":
+            tdls.gesv_batched(d["A"], d["B"], w.layout, out=(d["X"], d["piv"], d["info"]), **ex)
+        elif op == "getrf":
+            tdls.getrf_batched(d["A"], w.layout, out=(d["LU"], d["piv"], d["info"]), **ex)
+        elif op == "getrs":
+            tdls.getrs_batched(d["LU"], d["piv"], d["B"], w.layout, out=d["X"], **ex)
+        elif op == "potrf":
+            tdls.potrf_batched(d["A"], w.layout, out=(d["L"], d["info"]), **ex)
+        elif op == "potrs":
+            tdls.potrs_batched(d["L"], d["B"], w.layout, out=d["X"], **ex)
+        else:
+            tdls.posv_batched(d["A"], d["B"], w.layout, out=(d["X"], d["info"]), **ex)
+
+    # Buffer rotation: a working set below 512 MiB could be served from the
+    # 256 MB Infinity Cache when one launch follows another on the same
+    # buffers, so such workloads rotate over enough sets to exceed 512 MiB
+    # (at least 3); larger ones use one set.
+    sets = [make_set()]
+    ws_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
+    nsets = 1 if ws_bytes >= ROTATE_BELOW or args.no_rotate else \
+        min(4096, max(3, -(-ROTATE_BELOW // ws_bytes)))
+    sets += [make_set() for _ in range(nsets - 1)]
     torch.cuda.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    for i in range(args.warmup):
+        run(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # the timed region: exactly `steps` launches, one event pair around each
+    # (on the launch stream) for the per-launch kernel time
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        run(sets[i % nsets])
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    per_launch = np.array([a.elapsed_time(b) for a, b in evs])
+    kernel_ms = float(per_launch.mean())
     ms_per_step = wall * 1e3 / args.steps
+
+    # Secondary: synchronous API wall-clock per call (the ruSOLVER page's
+    # measure: output allocation, submission, execution and the wait; no
+    # upload or check), one sample per call
+    api = []
+    for i in range(args.api_samples):
+        d = sets[i % nsets]
+        t = time.perf_counter()
+        if op == "gesv":
+            tdls.gesv_batched(d["A"], d["B"], w.layout, **ex)
+        else:
+            run(d)
+        torch.cuda.synchronize()
+        api.append((time.perf_counter() - t) * 1e3)
+    d0 = sets[0]
+    A, B, X, piv, info = d0["A"], d0["B"], d0["X"], d0["piv"], d0["info"]
+    LU = d0.get("LU")
 
     # sanity of the timed output (no oracle here): status and a residual
     # sample (for getrf: the solve of the timed factors)
@@ -432,12 +648,22 @@ def main():
                    **({"gap_filtered": False} if "gap_filtered" in w.meta else {}),
                    "group_size": plan["group_size"], "systems_per_wave": plan["systems_per_wave"]},
         "kernel_ms": kernel_ms,
+        "kernel_ms_per_launch": {"mean": kernel_ms, "median": float(np.median(per_launch)),
+                                 "min": float(per_launch.min()), "max": float(per_launch.max()),
+                                 "launches": int(len(per_launch))},
+        "api_wall_ms": ({"median": float(np.median(api)), "min": float(min(api)),
+                         "max": float(max(api)), "samples": len(api)} if api else None),
+        "buffer_sets": {"sets": nsets, "working_set_bytes": int(ws_bytes),
+                        "rotated": nsets > 1},
         "hbm_gbs_algorithmic": achieved_gbs,
         "vector_tflops_algorithmic": achieved_tflops,
         "vector_frac": achieved_tflops / vec_peak,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(w.name, op)},
+        "issue_floor": issue_floor(w.name, op) if not args.batch and W == 1 else None,
+        "hbm_floor_ms": bytes_per_launch / (HBM_PEAK_GBS * 1e9) * 1e3,
+        "run": run_info(),
         "check": {"failed_systems": int((info_h != 0).sum()), "residual_max_sample": resid_max},
     }
     if not args.no_cpu:

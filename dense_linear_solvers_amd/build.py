@@ -30,7 +30,13 @@ COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract
 
 
 def library_path() -> str:
-    return os.path.join(BUILD, "libtdls.so")
+    """The library the binding loads: _build/libtdls.so, or the file named
+    by TDLS_LIB (the host-sanitized build, for CPU tests)."""
+    return os.environ.get("TDLS_LIB") or os.path.join(BUILD, "libtdls.so")
+
+
+def sanitized_library_path() -> str:
+    return os.path.join(BUILD, "libtdls_hostsan.so")
 
 
 def shapes() -> list:
@@ -98,9 +104,55 @@ def build(jobs: int = 0, verbose: bool = False, incremental: bool = False) -> st
     tmp = lib + ".tmp%d" % os.getpid()
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, lib)
+    _write_build_info()
     if verbose:
         print(f"linked {lib} in {time.time() - t0:.1f}s", flush=True)
     return lib
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The host side (argument checks, planner, dispatch: tdls_api.cpp)
+    rebuilt with AddressSanitizer and UndefinedBehaviorSanitizer (host code
+    only: -Xarch_host before each -fsanitize), linked with the kernel
+    objects of the last build into sanitized_library_path().  Load it with
+    TDLS_LIB and clang's ASan runtime preloaded."""
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    obj = os.path.join(BUILD, "obj", "tdls_api_hostsan.o")
+    _run([HIPCC, *COMMON, *san, "-x", "hip", "-c", os.path.join(CSRC, "tdls_api.cpp"),
+          "-o", obj])
+    objs = [os.path.join(BUILD, "obj", f"gesv_{sfx}_n{n}_r{nrhs}.o") for sfx, _, n, nrhs in shapes()]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError("build the library first; missing " + ", ".join(missing[:3]))
+    out = sanitized_library_path()
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", *san, *objs, obj,
+          "-o", out])
+    if verbose:
+        print(out)
+    return out
+
+
+def _write_build_info():
+    """_build/build_info.json: the source revision the library was built
+    from (git HEAD and whether the tree had changes), for measurement
+    records made where no repository is at hand."""
+    import json
+    root = os.path.dirname(HERE)
+    info = {"built_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
+    try:
+        head = subprocess.run(["git", "rev-parse", "HEAD"], cwd=root, stdout=subprocess.PIPE,
+                              stderr=subprocess.DEVNULL, text=True, timeout=10)
+        dirty = subprocess.run(["git", "status", "--porcelain", "--untracked-files=no"],
+                               cwd=root, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                               text=True, timeout=10)
+        if head.returncode == 0:
+            info["git_head"] = head.stdout.strip()
+            info["git_dirty"] = bool(dirty.stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(BUILD, "build_info.json"), "w", encoding="utf-8") as fh:
+        json.dump(info, fh)
 
 
 def clean():
@@ -108,5 +160,8 @@ def clean():
 
 
 if __name__ == "__main__":
-    inc = "--incremental" in sys.argv
-    print(build(verbose=True, incremental=inc))
+    if "--host-sanitize" in sys.argv:
+        print(build_host_sanitized(verbose=True))
+    else:
+        inc = "--incremental" in sys.argv
+        print(build(verbose=True, incremental=inc))
