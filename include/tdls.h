@@ -39,19 +39,30 @@ extern "C" {
 #endif
 
 /* Element type of A, B and X. */
-typedef enum tdls_dtype {
+/* In C++ the enumerations below take int as their underlying type, so any
+ * int passed through the C interface is a value of the type (the calls
+ * validate it and reject others with -i); without a fixed type an
+ * out-of-range value would be undefined behaviour in C++.  C enumerations
+ * are int-compatible already. */
+#ifdef __cplusplus
+#define TDLS_ENUM_BASE : int
+#else
+#define TDLS_ENUM_BASE
+#endif
+
+typedef enum tdls_dtype TDLS_ENUM_BASE {
   TDLS_F32 = 0, /* IEEE binary32, every operation in binary32 */
   TDLS_F64 = 1  /* IEEE binary64, every operation in binary64 */
 } tdls_dtype;
 
 /* Storage order of each system's A, B and X (the same flag for all three). */
-typedef enum tdls_layout {
+typedef enum tdls_layout TDLS_ENUM_BASE {
   TDLS_ROW_MAJOR = 0, /* A(r,c) at r*n + c;  B(r,j), X(r,j) at r*nrhs + j */
   TDLS_COL_MAJOR = 1  /* A(r,c) at c*n + r;  B(r,j), X(r,j) at j*n + r    */
 } tdls_layout;
 
 /* Operations, for tdls_plan_op. */
-typedef enum tdls_op {
+typedef enum tdls_op TDLS_ENUM_BASE {
   TDLS_OP_GESV = 0,  /* factor and solve in one call (tdls_gesv_batched) */
   TDLS_OP_GETRF = 1, /* factor only (tdls_getrf_batched) */
   TDLS_OP_GETRS = 2, /* solve from factors (tdls_getrs_batched) */
