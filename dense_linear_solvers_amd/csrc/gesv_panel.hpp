@@ -106,6 +106,18 @@ struct PanelShape {
   static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
 };
 
+// Row stride (elements) of rows staged through LDS, at most `cap`, a
+// multiple of the 16-byte vector: where possible one whose dword count is
+// 4 mod 8, so that eight lanes writing or reading 16 bytes each at the same
+// offset of eight consecutive rows start on eight different 4-bank groups
+// (no bank conflict); else the largest multiple of the vector that fits.
+constexpr int stage_stride(int cap, int es) {
+  const int vec = 16 / es;
+  for (int r = cap / vec * vec; r >= vec; r -= vec)
+    if ((r * es / 4) % 8 == 4) return r;
+  return cap / vec * vec;
+}
+
 // ---------------------------------------------------------------- lanes
 
 // Reduction over the T lanes of a group (groups are aligned, T | 64).
@@ -724,8 +736,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // (columns from the row's position on), the factorization all of L\U
       constexpr int EB = FACT ? 0 : KP * T;
       // row stride in LDS: a multiple of the vector width, not of 32 banks
-      constexpr int CM = S::GROUP_ELEMS / NS / VEC * VEC;
-      constexpr int RS = ((CM * (int)sizeof(Real) / 4) % 32 == 0 && CM > VEC) ? CM - VEC : CM;
+      constexpr int RS = stage_stride(S::GROUP_ELEMS / NS, (int)sizeof(Real));
       static_assert(RS >= VEC && NS * RS <= S::GROUP_ELEMS, "staging fits the group area");
       constexpr int NCH = (E - EB + RS - 1) / RS;
       auto ent = [&](auto Kc, auto ec) -> Real& {
@@ -1138,8 +1149,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       constexpr int Q0 = KL * T;                 // first position of the last slot
       constexpr int NS2 = N - Q0;                // its rows
       constexpr int E2 = N - Q0 + NRHS;          // entries moved per row
-      constexpr int CM2 = S::GROUP_ELEMS / NS2 / VEC * VEC;
-      constexpr int RS2 = ((CM2 * (int)sizeof(Real) / 4) % 32 == 0 && CM2 > VEC) ? CM2 - VEC : CM2;
+      constexpr int RS2 = stage_stride(S::GROUP_ELEMS / NS2, (int)sizeof(Real));
       static_assert(RS2 >= VEC && NS2 * RS2 <= S::GROUP_ELEMS, "staging fits the group area");
       constexpr int NCH2 = (E2 + RS2 - 1) / RS2;
       auto ent2 = [&](auto ec) -> Real& {
