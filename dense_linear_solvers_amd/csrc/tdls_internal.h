@@ -72,18 +72,23 @@ struct LaunchPlan {
 };
 
 // Group size chosen at compile time for each instantiation: the smallest of
-// 4, 16, 64 lanes whose rows fit a register budget.  Registers per lane for
-// the data rows are R * (N + NRHS) * (element size / 4) with R = ceil(N / T);
-// fewer lanes per system means more systems share each wave's pivot search,
-// divisions and exchanges.  4 and 16 lanes are DPP broadcast domains (quad,
-// row); 64 lanes is the whole wave.
+// 4, 16, 64 lanes whose rows fit a register budget (4 lanes up to N = 24).
+// Registers per lane for the data rows are R * (N + NRHS) * (element size /
+// 4) with R = ceil(N / T); fewer lanes per system means more systems share
+// each wave's pivot search, divisions and exchanges, and fewer phantom rows
+// (N = 24 in 16-lane groups pads its second slot with 8 of them).  4 and 16
+// lanes are DPP broadcast domains (quad, row); 64 lanes is the whole wave.
+// Measured at N = 24 float32 on 1,000,000 row-major systems, 16 -> 4 lanes:
+// gesv 1.18 -> 0.85 ms (one right-hand side) and 1.24 -> 0.95 ms (two),
+// getrf 1.23 -> 1.07, potrf 1.31 -> 1.00, posv 1.02 -> 0.57, potrs 0.62 ->
+// 0.51 ms, at two waves per SIMD against five.
 constexpr int kRegBudget = 160;
 constexpr int rows_per_lane(int N, int T) { return (N + T - 1) / T; }
 constexpr int row_regs(int N, int NRHS, int T, bool is64) {
   return rows_per_lane(N, T) * (N + NRHS) * (is64 ? 2 : 1);
 }
 constexpr int pick_group_size(int N, int NRHS, bool is64) {
-  if (N <= 16 && row_regs(N, NRHS, 4, is64) <= kRegBudget) return 4;
+  if (N <= 24 && row_regs(N, NRHS, 4, is64) <= kRegBudget) return 4;
   if (row_regs(N, NRHS, 16, is64) <= kRegBudget) return 16;
   return 64;
 }
@@ -110,10 +115,13 @@ constexpr int alt_group_size(int N, int NRHS, bool is64) {
 // 0.059 ms and 1.29 -> 0.95 ms (nrhs = 4), getrs 0.81 -> 0.62 ms, getrf
 // even.  The Cholesky kernels keep the quad (potrf 0.94 against 1.14 ms,
 // posv 0.68 against 1.07 ms at the larger batch); at N = 8 and in float32
-// the quad is ahead for every operation.
+// the quad is ahead for every operation but getrs at N = 24 (six rows per
+// lane), which keeps the 16-lane group: 0.48 against 0.49 ms with one
+// right-hand side, 0.53 against 0.58 ms with two (1,000,000 systems).
 constexpr bool lu_prefers_wider(int op, int N, bool is64, int T0, int T1) {
-  return is64 && N == 16 && T0 == 4 && T1 == 16 &&
-         (op == kOpGesv || op == kOpGetrf || op == kOpGetrs);
+  if (T0 != 4 || T1 != 16) return false;
+  if (is64 && N == 16) return op == kOpGesv || op == kOpGetrf || op == kOpGetrs;
+  return !is64 && N == 24 && op == kOpGetrs;
 }
 
 // Panel width of the factorization (columns whose pivot rows are exchanged

@@ -349,7 +349,8 @@ def test_potrs_validation_before_launch(lib):
 
 def test_group_size_choice_per_op(lib):
     """LU in float64 at n = 16 runs 16-lane groups at every batch size; the
-    Cholesky kernels and float32 keep 4-lane groups there (large batches)."""
+    Cholesky kernels and float32 keep 4-lane groups there (large batches),
+    and float32 takes them up to n = 24 where the rows fit."""
     big = 1 << 20
     for n in (9, 16):
         for op in ("getrf", "getrs"):
@@ -359,6 +360,18 @@ def test_group_size_choice_per_op(lib):
             assert tdls.plan_op(op, "f64", "row", n, 1, big)["group_size"] == 4
         assert tdls.plan_gesv("f32", "row", n, 4, big)["group_size"] == 4
     assert tdls.plan_gesv("f64", "row", 8, 1, big)["group_size"] == 4
+    # float32 at n = 17..24: quads where six rows per lane fit (one or two
+    # right-hand sides), except getrs; 16-lane groups with more right-hand sides
+    for n in (17, 24):
+        for nrhs in (1, 2):
+            assert tdls.plan_gesv("f32", "row", n, nrhs, big)["group_size"] == 4
+            for op in ("posv", "potrs"):
+                assert tdls.plan_op(op, "f32", "row", n, nrhs, big)["group_size"] == 4
+            assert tdls.plan_op("getrs", "f32", "row", n, nrhs, big)["group_size"] == 16
+        for op in ("getrf", "potrf"):
+            assert tdls.plan_op(op, "f32", "row", n, 1, big)["group_size"] == 4
+        assert tdls.plan_gesv("f32", "row", n, 4, big)["group_size"] == 16
+        assert tdls.plan_gesv("f64", "row", n, 1, big)["group_size"] == 16
 
 
 def test_out_tensors_are_checked_before_any_call():
