@@ -71,6 +71,21 @@ def algorithmic_bytes(n: int, nrhs: int, es: int, op: str = "gesv") -> int:
     return n * n * es + 2 * n * nrhs * es + 4 * n + 4
 
 
+def triangle_line_bytes(n: int, nrhs: int, es: int, layout: str) -> int:
+    """potrs per system, priced by the 128-byte lines its input forces: the
+    lines of a contiguous n x n matrix (the batch starts line-aligned and
+    n*n*es is a multiple of 128 for every kernel size) that hold part of
+    the lower triangle, plus B read and X written.  Reading a triangle out
+    of a dense matrix fetches whole lines, so this is the traffic a potrs of
+    this layout cannot avoid."""
+    lines = set()
+    for i in range(n):
+        for j in range(i + 1):
+            off = (j * n + i if layout == "col" else i * n + j) * es
+            lines.add(off // 128)
+    return len(lines) * 128 + 2 * n * nrhs * es
+
+
 def algorithmic_flops(n: int, nrhs: int, op: str = "gesv") -> int:
     """Per system: elimination 2*sum(m^2) multiply-add flops plus sum(m)
     divisions (m = n-1 .. 1), forward and back substitution on nrhs columns
@@ -136,6 +151,15 @@ def read_traffic(path: str) -> dict:
             k, v = line.rstrip("\n").split(" = ", 1)
             d[k] = v
     return d
+
+
+def _line_bytes_entry(w, es: int, kernel_ms: float) -> dict:
+    """potrs against the whole lines its triangle occupies (see
+    triangle_line_bytes), next to the triangle-only roofline."""
+    per = triangle_line_bytes(w.n, w.nrhs, es, w.layout)
+    gbs = per * w.batch / (kernel_ms * 1e-3) / 1e9
+    return {"bytes_per_system": per, "vs_triangle": per / algorithmic_bytes(w.n, w.nrhs, es, "potrs"),
+            "achieved": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
 def measured_traffic(workload: str, op: str = "gesv"):
@@ -706,6 +730,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(w.name, op)},
+        **({"potrs_line_bytes": _line_bytes_entry(w, es, kernel_ms)} if op == "potrs" and W == 1
+           else {}),
         "issue_floor": issue_floor(w.name, op) if not args.batch and W == 1 else None,
         "hbm_floor_ms": bytes_per_launch / (HBM_PEAK_GBS * 1e9) * 1e3,
         "run": run_info(),
