@@ -211,21 +211,46 @@ def summarize_counters(workload: str, op: str, fetch_dir: str, write_dir: str,
          "fetch_scale": fetch_scale, "write_scale": write_scale,
          "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
          "hbm_bytes_per_launch": fetch_b + write_b}
-    # the summary's comment lines (commands, calibration, the figures in
-    # words) stay; the data lines below the marker are replaced
     out = traffic_path(workload, op)
-    head = [f"# HBM traffic of {kern} ({op}) on {workload}: rocprofv3 FETCH_SIZE and "
-            "WRITE_SIZE per dispatch, each scaled by the same counter on a plain copy",
+    from dense_linear_solvers_amd.workloads import RECIPES
+    r = RECIPES.get(workload)
+    es = 8 if (r is not None and r.dtype == "f64") else 4
+    algo = algorithmic_bytes(r.n, r.nrhs, es, op) * r.batch if r is not None else None
+    pre = f"gpurun_out/pf/{op}_{workload}"
+    cmd = f"python3 bench.py --workload {workload} --op {op} --no-cpu --steps 3 --warmup 1"
+    head = [f"# HBM traffic of {kern} ({op}) on {workload}: rocprofv3 FETCH_SIZE and WRITE_SIZE per "
+            "dispatch, each scaled by the same counter on a plain copy",
+            "# commands (repository root, one MI355X), each counter in a run of its own:",
+            f"#   rocprofv3 --pmc FETCH_SIZE -T -d {pre}_FETCH_SIZE -o t -f csv -- {cmd}",
+            f"#   rocprofv3 --pmc WRITE_SIZE -T -d {pre}_WRITE_SIZE -o t -f csv -- {cmd}",
+            "#   rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pf/copy_FETCH_SIZE -o t -f csv -- "
+            "python3 bench.py --calibrate-copy",
+            "#   rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pf/copy_WRITE_SIZE -o t -f csv -- "
+            "python3 bench.py --calibrate-copy",
+            f"#   python3 bench.py --workload {workload} --op {op} --summarize-counters "
+            f"{pre}_FETCH_SIZE {pre}_WRITE_SIZE gpurun_out/pf/copy_FETCH_SIZE "
+            "gpurun_out/pf/copy_WRITE_SIZE",
+            "#",
+            f"# calibration: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE = {cf:.0f} KiB and "
+            f"WRITE_SIZE = {cw:.0f} KiB: fetch scale {fetch_scale:.4f}, write scale {write_scale:.4f}",
+            f"# {kern} (median over dispatches): FETCH_SIZE {fk:.0f} KiB, WRITE_SIZE {wk:.0f} KiB; "
+            f"scaled: read {fetch_b:.4e} B, write {write_b:.4e} B, total {fetch_b + write_b:.4e} B "
+            "per launch" + (f" against {algo:.4e} B algorithmic "
+                            f"({100 * ((fetch_b + write_b) / algo - 1):+.1f}%)" if algo else ""),
             TRAFFIC_MARKER]
-    if os.path.exists(out):
-        with open(out, encoding="utf-8") as fh:
-            old = fh.read().splitlines()
-        if TRAFFIC_MARKER in old:
-            head = old[:old.index(TRAFFIC_MARKER) + 1]
     with open(out, "w", encoding="utf-8") as fh:
         fh.write("\n".join(head + traffic_lines(d)) + "\n")
         fh.write("\n")
     return d
+
+
+# the two SQ counter passes (eight SQ counters at most per rocprofv3 run)
+SQ_PASSES = {
+    "sqa": "SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+           "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA",
+    "sqb": "SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
+           "SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES SQ_IFETCH",
+}
 
 
 def sq_path(workload: str, op: str) -> str:
@@ -266,13 +291,22 @@ def summarize_sq(workload: str, op: str, dirs: list) -> dict:
     if q is not None:
         d["valu_floor_ms"] = waves * q * 4 / SIMDS / (CLOCK_GHZ * 1e6)
     out = sq_path(workload, op)
-    head = [f"# SQ counters of {kern} ({op}) on {workload}, per wave (median over dispatches)",
-            TRAFFIC_MARKER]
-    if os.path.exists(out):
-        with open(out, encoding="utf-8") as fh:
-            old = fh.read().splitlines()
-        if TRAFFIC_MARKER in old:
-            head = old[:old.index(TRAFFIC_MARKER) + 1]
+    cmd = f"python3 bench.py --workload {workload} --op {op} --no-cpu --steps 3 --warmup 1"
+    head = [f"# SQ counters of {kern} ({op}) on {workload}: per wave, the median over dispatches of "
+            "each counter's per-dispatch total divided by the waves of a launch (grid threads / 64).",
+            "# SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* count quad-cycles (4 clock cycles); "
+            "SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE and SQ_BUSY_CYCLES count clock cycles "
+            "(SQ_BUSY_CYCLES per shader engine).",
+            "# valu_floor_ms = waves x SQ_ACTIVE_INST_VALU x 4 cycles / 1024 SIMDs / 2.4 GHz.",
+            "# commands (repository root, one MI355X), one pass each:"]
+    for d_ in dirs:
+        tag = os.path.basename(os.path.normpath(d_))
+        cs = (SQ_PASSES.get(tag[-3:]) if tag[-3:] in SQ_PASSES else None)
+        if cs:
+            head.append(f"#   rocprofv3 --pmc {cs} -T -d gpurun_out/pf/{tag} -o t -f csv -- {cmd}")
+    head += [f"#   python3 bench.py --workload {workload} --op {op} --summarize-sq "
+             + " ".join(f"gpurun_out/pf/{os.path.basename(os.path.normpath(d_))}" for d_ in dirs),
+             TRAFFIC_MARKER]
     with open(out, "w", encoding="utf-8") as fh:
         fh.write("\n".join(head + traffic_lines(d)) + "\n")
     return d
