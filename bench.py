@@ -212,8 +212,8 @@ def summarize_counters(workload: str, op: str, fetch_dir: str, write_dir: str,
          "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
          "hbm_bytes_per_launch": fetch_b + write_b}
     out = traffic_path(workload, op)
-    from dense_linear_solvers_amd.workloads import RECIPES
-    r = RECIPES.get(workload)
+    from dense_linear_solvers_amd.workloads import RECIPES, SPD_RECIPES
+    r = RECIPES.get(workload) or SPD_RECIPES.get(workload)
     es = 8 if (r is not None and r.dtype == "f64") else 4
     algo = algorithmic_bytes(r.n, r.nrhs, es, op) * r.batch if r is not None else None
     pre = f"gpurun_out/pf/{op}_{workload}"
