@@ -462,14 +462,16 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     } else {
       // ---- several right-hand sides: both triangular solves run after the
       // factorization in the column-class / row-phase layout of the LU
-      // path, one division per column class per step, L read from a
-      // row-packed lower triangle in LDS (row i at i (i + 1) / 2).
+      // path (a class is P consecutive lanes, lane j0 * P + ph; y_k and x_k
+      // reach their class by DPP), one division per column class per step,
+      // L read from a row-packed lower triangle in LDS (row i at
+      // i (i + 1) / 2).
       constexpr int NJ = NRHS < T ? NRHS : T;
       constexpr int P = T / NJ;
       constexpr int JR = NRHS / NJ;
       constexpr int QR = (N + P - 1) / P;
-      const int j0 = tx % NJ;
-      const int ph = tx / NJ;
+      const int j0 = tx / P;   // column class: P consecutive lanes
+      const int ph = tx % P;
       const int gb = g * T;
       auto ltri = [](int i) { return i * (i + 1) / 2; };
       sfor<0, R>([&](auto Kc) {
@@ -533,8 +535,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           Real yb;
           if constexpr (P == 1)
             yb = yk;
+          else if constexpr (P <= 16)
+            yb = class_bcast<P, kp>(yk);   // lane kp of the class, by DPP
           else
-            yb = lane_fetch_any(yk, gb + kp * NJ + j0);
+            yb = lane_fetch_any(yk, gb + j0 * P + kp);
           sfor<km, QR>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             yv[m][jj] = fma_r(-lik[m], yb, yv[m][jj]);
@@ -562,8 +566,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
           Real xb;
           if constexpr (P == 1)
             xb = x;
+          else if constexpr (P <= 16)
+            xb = class_bcast<P, kp>(x);   // lane kp of the class, by DPP
           else
-            xb = lane_fetch_any(x, gb + kp * NJ + j0);
+            xb = lane_fetch_any(x, gb + j0 * P + kp);
           sfor<0, km + 1>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             yv[m][jj] = fma_r(-lkq[m], xb, yv[m][jj]);

@@ -1,6 +1,7 @@
 // Batched gesv, panel kernel: LU with partial row pivoting plus forward and
-// back substitution, one n x n system per group of T lanes (T = 4, 16, 32, 64)
-// of a wave64, rows held in VGPRs.
+// back substitution, one n x n system per group of T lanes of a wave64
+// (T = 4, 16 or 64 as the planner picks; the templates also take T = 32,
+// which was measured slower and is not planned), rows held in VGPRs.
 //
 // What is computed (cited by page title and section):
 //  * "solver_static.hpp File Reference" (TDLS CooperativeLUpp), Detailed
@@ -185,6 +186,46 @@ __device__ __forceinline__ float lane_fetch_any(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
+// 32-bit value of `x` held by lane KP of this lane's class, a class being
+// CL consecutive lanes (CL = 2, 4, 8 or 16, aligned to CL): a quad permute
+// for classes inside a quad, a broadcast from a fixed lane of each 16-lane
+// row otherwise (half rows take two, one per pair of 4-lane banks).  The
+// source may have been written by the instruction just before (two wait
+// states before the DPP read).
+template <int CL, int KP>
+__device__ __forceinline__ uint32_t class_bcast_u32(uint32_t x) {
+  static_assert(CL == 2 || CL == 4 || CL == 8 || CL == 16, "class of 2, 4, 8 or 16 lanes");
+  static_assert(KP >= 0 && KP < CL, "source lane inside the class");
+  uint32_t out;
+  if constexpr (CL <= 4) {
+    constexpr int q0 = KP, q1 = CL == 4 ? KP : 2 + KP;
+    constexpr int qp = q0 | (q0 << 2) | (q1 << 4) | (q1 << 6);
+    out = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, qp, 0xf, 0xf, false);
+  } else if constexpr (CL == 8) {
+    asm volatile(
+        "s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0x3\n\t"
+        "v_mov_b32_dpp %0, %1 row_newbcast:%3 row_mask:0xf bank_mask:0xc"
+        : "=&v"(out)
+        : "v"(x), "i"(KP), "i"(8 + KP));
+  } else {
+    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+                 : "=v"(out)
+                 : "v"(x), "i"(KP));
+  }
+  return out;
+}
+template <int CL, int KP>
+__device__ __forceinline__ double class_bcast(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = class_bcast_u32<CL, KP>((uint32_t)b);
+  const uint32_t hi = class_bcast_u32<CL, KP>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int CL, int KP>
+__device__ __forceinline__ float class_bcast(float x) {
+  return __builtin_bit_cast(float, class_bcast_u32<CL, KP>(__builtin_bit_cast(uint32_t, x)));
+}
+
 // 32-bit value of `x` held by lane `src` (absolute lane index) of this wave;
 // `src` is wave-uniform when T = 64.
 template <int T>
@@ -352,10 +393,11 @@ __device__ __forceinline__ int utri_row(int q) { return q * N - q * (q - 1) / 2;
 // right-hand side: lane tx holds the positions tx + K*T, x_k is formed on
 // lane k % T and reaches the rows above by DPP inside the FMA (a lane fetch
 // for groups wider than a 16-lane row).  Several: the group's lanes split
-// into NJ column classes and P row phases; lane (ph, j0) holds the columns
+// into NJ column classes and P row phases; lane j0 * P + ph holds the columns
 // j = j0 + NJ*jj of the positions ph + P*m, so x_k costs one division per
 // column class on the lanes of phase k % P, handed to the lanes of the same
-// class by a lane fetch; U(q, k) is read from the store.
+// class by DPP (classes are P consecutive lanes); U(q, k) is read from the
+// store.
 template <typename Real, int N, int NRHS, int T, bool ZERO_NONFINITE = true, typename WR,
           typename WU>
 __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, bool live,
@@ -373,8 +415,8 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
   constexpr int P = NRHS == 1 ? T : T / NJ;
   constexpr int JR = NRHS / NJ;
   constexpr int QR = (N + P - 1) / P;
-  const int j0 = NRHS == 1 ? 0 : tx % NJ;
-  const int ph = NRHS == 1 ? tx : tx / NJ;
+  const int j0 = NRHS == 1 ? 0 : tx / P;   // column class: P consecutive lanes
+  const int ph = NRHS == 1 ? tx : tx % P;
   Real yv[QR][JR];
   sfor<0, QR>([&](auto mc) {
     constexpr int m = decltype(mc)::value;
@@ -451,11 +493,13 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
     }
   } else {
     // Several right-hand sides: the group's lanes split into NJ column
-    // classes and P row phases.  Lane (ph, j0) holds the right-hand-side
-    // columns j = j0 + NJ*jj of the positions q = ph + P*m, so each x_k is
-    // one division per column on the NJ lanes of phase k % P, handed to the
-    // lanes of the same column class by a lane fetch; every lane then folds
-    // it into its rows, reading u(q, k) from the triangular store.
+    // classes of P consecutive lanes (lane j0 * P + ph is phase ph of class
+    // j0).  It holds the right-hand-side columns j = j0 + NJ*jj of the
+    // positions q = ph + P*m, so each x_k is one division per column on the
+    // NJ lanes of phase k % P, handed to the other lanes of its class by a
+    // DPP broadcast (a lane fetch for classes wider than a 16-lane row);
+    // every lane then folds it into its rows, reading u(q, k) from the
+    // triangular store.
     Real xr[QR][JR];
     sfor<0, QR>([&](auto mc) {
       sfor<0, JR>([&](auto jc) { xr[decltype(mc)::value][decltype(jc)::value] = Real(0); });
@@ -470,7 +514,6 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
         constexpr int m = decltype(mc)::value;
         uk[m] = rw[m][k];   // u(q, k) of row q = ph + P*m (meaningful for q <= k)
       });
-      const int src = gbase + kp * NJ + j0;   // the lane of phase kp, same column class
       sfor<0, JR>([&](auto jc) {
         constexpr int jj = decltype(jc)::value;
         const Real x = yv[km][jj] / uk[km];   // meaningful on the lanes of phase kp
@@ -479,8 +522,10 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
         Real xk;
         if constexpr (P == 1)
           xk = x;   // every lane is the owner of its own column class
+        else if constexpr (P <= 16)
+          xk = class_bcast<P, kp>(x);   // lane kp of the class, by DPP
         else
-          xk = lane_fetch_any(x, src);
+          xk = lane_fetch_any(x, gbase + j0 * P + kp);
         sfor<0, km + 1>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
           yv[m][jj] = fma_r(-uk[m], xk, yv[m][jj]);

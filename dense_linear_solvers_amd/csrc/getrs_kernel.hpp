@@ -236,9 +236,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
   if constexpr (S::CLASSES) {
     // ---- several right-hand sides: both substitutions in the column-class
     // / row-phase layout of the back substitution of the LU kernel (lane
-    // (ph, j0) holds the right-hand-side columns j0 + NJ*jj of the positions
-    // ph + P*m), so a step costs one division per column class rather than
-    // NRHS divisions on one lane.  The forward substitution reads L from a
+    // j0 * P + ph holds the right-hand-side columns j0 + NJ*jj of the
+    // positions ph + P*m; a class is P consecutive lanes, so y_k reaches its
+    // class by DPP), so a step costs one division per column class rather
+    // than NRHS divisions on one lane.  The forward substitution reads L from a
     // row-packed lower triangle in LDS (row i at i (i + 1) / 2, unit
     // diagonal implied); the back substitution is the LU kernel's.
     Real* ws = reinterpret_cast<Real*>(glds + S::PIV_BYTES);
@@ -246,8 +247,8 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     constexpr int P = T / NJ;
     constexpr int JR = NRHS / NJ;
     constexpr int QR = (N + P - 1) / P;
-    const int j0 = tx % NJ;
-    const int ph = tx / NJ;
+    const int j0 = tx / P;   // column class: P consecutive lanes
+    const int ph = tx % P;
     auto ltri = [](int i) { return i * (i + 1) / 2; };
     sfor<0, R>([&](auto Kc) {
       constexpr int K = decltype(Kc)::value;
@@ -306,8 +307,10 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
         Real yb;
         if constexpr (P == 1)
           yb = yv[km][jj];
+        else if constexpr (P <= 16)
+          yb = class_bcast<P, kp>(yv[km][jj]);   // lane kp of the class, by DPP
         else
-          yb = lane_fetch_any(yv[km][jj], gbase + kp * NJ + j0);
+          yb = lane_fetch_any(yv[km][jj], gbase + j0 * P + kp);
         sfor<km, QR>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
           yv[m][jj] = fma_r(-lik[m], yb, yv[m][jj]);
