@@ -446,19 +446,28 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
     // (every entry is assigned at its own step)
     Real xr[R];
     sfor<0, R>([&](auto Kc) { xr[decltype(Kc)::value] = Real(0); });
+    // u(q, k) of this lane's rows, read one step ahead (two buffers) so that
+    // a step's LDS reads overlap the step before; each step's instructions
+    // stay together (hoisting every read ahead of the loop costs registers)
+    Real ub[2][R];
+    auto read_u = [&](auto icc) {
+      constexpr int k2 = N - 1 - decltype(icc)::value;
+      sfor<0, k2 / T + 1>([&](auto Kc) {
+        constexpr int K = decltype(Kc)::value;
+        ub[decltype(icc)::value % 2][K] = rw[K][k2];
+      });
+    };
+    read_u(std::integral_constant<int, 0>{});
     sfor<0, N>([&](auto ic) {
       constexpr int k = N - 1 - decltype(ic)::value;
       constexpr int kl = k % T;
       constexpr int ks = k / T;
       constexpr int SLK = kl % (T < 16 ? T : 16);   // lane of k inside its DPP domain
-      // keep the U reads of one step together with their use (hoisting them
-      // all ahead of the loop costs registers, not latency)
+      constexpr int cur = decltype(ic)::value % 2;
       __builtin_amdgcn_sched_barrier(0);
-      Real uk[ks + 1];
-      sfor<0, ks + 1>([&](auto Kc) {
-        constexpr int K = decltype(Kc)::value;
-        uk[K] = rw[K][k];   // u(q, k) of this lane's row q in slot K
-      });
+      if constexpr (decltype(ic)::value + 1 < N)
+        read_u(std::integral_constant<int, decltype(ic)::value + 1>{});
+      Real(&uk)[R] = ub[cur];
       const Real x = yv[ks][0] / uk[ks];   // meaningful on lane kl
       xr[ks] = tx == kl ? x : xr[ks];
       asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
@@ -504,16 +513,25 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
     sfor<0, QR>([&](auto mc) {
       sfor<0, JR>([&](auto jc) { xr[decltype(mc)::value][decltype(jc)::value] = Real(0); });
     });
+    // u(q, k) of this lane's rows, read one step ahead as above
+    Real ub[2][QR];
+    auto read_u = [&](auto icc) {
+      constexpr int k2 = N - 1 - decltype(icc)::value;
+      sfor<0, k2 / P + 1>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        ub[decltype(icc)::value % 2][m] = rw[m][k2];   // u(q, k2), q = ph + P*m
+      });
+    };
+    read_u(std::integral_constant<int, 0>{});
     sfor<0, N>([&](auto ic) {
       constexpr int k = N - 1 - decltype(ic)::value;
       constexpr int kp = k % P;
       constexpr int km = k / P;
+      constexpr int cur = decltype(ic)::value % 2;
       __builtin_amdgcn_sched_barrier(0);
-      Real uk[km + 1];
-      sfor<0, km + 1>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        uk[m] = rw[m][k];   // u(q, k) of row q = ph + P*m (meaningful for q <= k)
-      });
+      if constexpr (decltype(ic)::value + 1 < N)
+        read_u(std::integral_constant<int, decltype(ic)::value + 1>{});
+      Real(&uk)[QR] = ub[cur];   // meaningful for q <= k
       sfor<0, JR>([&](auto jc) {
         constexpr int jj = decltype(jc)::value;
         const Real x = yv[km][jj] / uk[km];   // meaningful on the lanes of phase kp
