@@ -513,16 +513,29 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       wave_sync_lds();
       // L y = b: y_k / L(k,k) on the lanes of phase k % P, then y_k leaves
       // the rows below it (rows at or above k are final and keep their value)
+      // L(i, k) of this lane's rows (L(k,k) on the lanes of phase k % P)
+      // read one step ahead, two register buffers, so that a step's LDS
+      // reads overlap the step before; likewise L(k, q) below
+      Real lb[2][QR];
+      auto read_l = [&](auto kcc) {
+        constexpr int k2 = decltype(kcc)::value;
+        sfor<k2 / P, QR>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          lb[k2 % 2][m] = lrow[m][k2];   // L(i, k2), i = ph + P*m (meaningful for i >= k2)
+        });
+      };
+      read_l(std::integral_constant<int, 0>{});
       sfor<0, N>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         constexpr int kp = k % P;
         constexpr int km = k / P;
         __builtin_amdgcn_sched_barrier(0);
-        const Real lkk = lrow[km][k];   // L(k,k) on the lanes of phase kp
+        if constexpr (k + 1 < N) read_l(std::integral_constant<int, k + 1>{});
+        const Real lkk = lb[k % 2][km];   // L(k,k) on the lanes of phase kp
         Real lik[QR];
         sfor<km, QR>([&](auto mc) {
           constexpr int m = decltype(mc)::value;
-          const Real v = lrow[m][k];    // L(i,k), i = ph + P*m (meaningful for i > k)
+          const Real v = lb[k % 2][m];    // L(i,k), i = ph + P*m (meaningful for i > k)
           if constexpr (m == km)
             lik[m] = ph > kp ? v : Real(0);
           else
@@ -547,17 +560,27 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       });
       // L^T x = y: x_k = y_k / L(k,k) on the lanes of phase k % P, removed
       // from the rows above with L(k, q) (rows at or below k are done)
+      Real qb[2][QR + 1];   // [QR]: L(k,k)
+      auto read_q = [&](auto icc) {
+        constexpr int k2 = N - 1 - decltype(icc)::value;
+        qb[decltype(icc)::value % 2][QR] = lrow[k2 / P][k2];
+        sfor<0, k2 / P + 1>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          qb[decltype(icc)::value % 2][m] =
+              sq[ltri(k2) + (ph + P * m < N ? ph + P * m : N - 1)];   // L(k2, q)
+        });
+      };
+      read_q(std::integral_constant<int, 0>{});
       sfor<0, N>([&](auto ic) {
         constexpr int k = N - 1 - decltype(ic)::value;
         constexpr int kp = k % P;
         constexpr int km = k / P;
+        constexpr int cur = decltype(ic)::value % 2;
         __builtin_amdgcn_sched_barrier(0);
-        const Real lkk = lrow[km][k];
-        Real lkq[km + 1];
-        sfor<0, km + 1>([&](auto mc) {
-          constexpr int m = decltype(mc)::value;
-          lkq[m] = sq[ltri(k) + (ph + P * m < N ? ph + P * m : N - 1)];   // L(k, q)
-        });
+        if constexpr (decltype(ic)::value + 1 < N)
+          read_q(std::integral_constant<int, decltype(ic)::value + 1>{});
+        const Real lkk = qb[cur][QR];
+        Real(&lkq)[QR + 1] = qb[cur];
         sfor<0, JR>([&](auto jc) {
           constexpr int jj = decltype(jc)::value;
           const Real x = yv[km][jj] / lkk;   // meaningful on the lanes of phase kp

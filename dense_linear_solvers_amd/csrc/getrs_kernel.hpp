@@ -288,15 +288,27 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
     wave_sync_lds();
     // L y = P b: y_k (final on the lanes of phase k % P) leaves the rows
     // below it
+    // L(i, k) of this lane's rows read one step ahead (two register
+    // buffers), so a step's LDS reads overlap the step before
+    Real lb[2][QR];
+    auto read_l = [&](auto kcc) {
+      constexpr int k2 = decltype(kcc)::value;
+      sfor<k2 / P, QR>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        lb[k2 % 2][m] = lrow[m][k2];   // L(i, k2), i = ph + P*m (meaningful for i > k2)
+      });
+    };
+    read_l(std::integral_constant<int, 0>{});
     sfor<0, N - 1>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       constexpr int kp = k % P;
       constexpr int km = k / P;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k + 1 < N - 1) read_l(std::integral_constant<int, k + 1>{});
       Real lik[QR];
       sfor<km, QR>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
-        const Real v = lrow[m][k];    // L(i, k), i = ph + P*m (meaningful for i > k)
+        const Real v = lb[k % 2][m];
         if constexpr (m == km)
           lik[m] = ph > kp ? v : Real(0);
         else
