@@ -67,6 +67,38 @@ __device__ __forceinline__ double fma_r(double a, double b, double c) { return _
 __device__ __forceinline__ float fabs_r(float v) { return __builtin_fabsf(v); }
 __device__ __forceinline__ double fabs_r(double v) { return __builtin_fabs(v); }
 
+// float64 division with the divisor's reciprocal formed ahead of time.
+// The IEEE quotient n / d is what the compiler's division sequence computes:
+// scale d and n (v_div_scale), a reciprocal of the scaled d refined by two
+// Newton-Raphson steps, q = n r, the residual e = fma(-d, q, n), q' =
+// fma(e, r, q) (v_div_fmas), then the special cases (v_div_fixup).  When
+// neither operand is scaled (the scale steps return them unchanged, no
+// scaling flag) and the fix-up leaves q' unchanged, the quotient is q'
+// computed from the same reciprocal: recip_div64 forms that reciprocal from
+// d alone, quot_div64 the quotient in three dependent operations, and
+// quot_div64_exact tells afterwards whether the shortcut was the sequence's
+// own result (else the caller divides).
+__device__ __forceinline__ double recip_div64(double d) {
+  double r = __builtin_amdgcn_rcp(d);
+  double e = __builtin_fma(-d, r, 1.0);
+  r = __builtin_fma(r, e, r);
+  e = __builtin_fma(-d, r, 1.0);
+  return __builtin_fma(r, e, r);
+}
+__device__ __forceinline__ double quot_div64(double n, double d, double r) {
+  const double q = n * r;
+  return __builtin_fma(__builtin_fma(-d, q, n), r, q);
+}
+__device__ __forceinline__ bool quot_div64_exact(double n, double d, double x) {
+  bool fd, fn;
+  const double ds = __builtin_amdgcn_div_scale(n, d, false, &fd);
+  const double ns = __builtin_amdgcn_div_scale(n, d, true, &fn);
+  const double fx = __builtin_amdgcn_div_fixup(x, d, n);
+  return (__builtin_bit_cast(uint64_t, ds) == __builtin_bit_cast(uint64_t, d)) &
+         (__builtin_bit_cast(uint64_t, ns) == __builtin_bit_cast(uint64_t, n)) & !fn &
+         (__builtin_bit_cast(uint64_t, fx) == __builtin_bit_cast(uint64_t, x));
+}
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void sfor(F&& f) {
   if constexpr (B < E) {
@@ -1241,19 +1273,73 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
       // Description, the solution entry kept by its owner)
       Real xr[R];
       sfor<0, R>([&](auto Kc) { xr[decltype(Kc)::value] = Real(0); });
-      sfor<0, N>([&](auto ic) {
-        constexpr int k = N - 1 - decltype(ic)::value;
-        constexpr int kl = k % T;
-        constexpr int ks = k / T;
-        constexpr int SLK = kl % SL;
-        const Real x = y[ks][0] / a[ks][k];   // meaningful on lane kl
-        xr[ks] = tx == kl ? x : xr[ks];
-        asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
-        sfor<0, ks + 1>([&](auto Kc) {
-          constexpr int K = decltype(Kc)::value;
-          fnmac_bcast<T, SLK, K == 0>(y[K][0], x, a[K][k]);
+      auto solve_divide = [&]() __attribute__((always_inline)) {
+        sfor<0, N>([&](auto ic) {
+          constexpr int k = N - 1 - decltype(ic)::value;
+          constexpr int kl = k % T;
+          constexpr int ks = k / T;
+          constexpr int SLK = kl % SL;
+          const Real x = y[ks][0] / a[ks][k];   // meaningful on lane kl
+          xr[ks] = tx == kl ? x : xr[ks];
+          asm volatile("" : "+v"(xr[ks]));   // select now, not at the store
+          sfor<0, ks + 1>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            fnmac_bcast<T, SLK, K == 0>(y[K][0], x, a[K][k]);
+          });
         });
-      });
+      };
+      if constexpr (is64) {
+        // float64: every lane forms the reciprocal of its own rows' diagonal
+        // (slot K holds position K*T + tx) before the chain starts, so each
+        // step costs three dependent operations instead of the division
+        // sequence; afterwards each lane checks the steps it owned
+        // (quot_div64_exact) and a wave with any miss solves again by
+        // division from the saved right-hand sides (the same bits either way)
+        double dg[R], rinv[R];
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          constexpr int c0 = K * T < N ? K * T : N - 1;
+          constexpr int c1 = (K + 1) * T < N ? (K + 1) * T : N;
+          double d = a[K][c0];
+          sfor<c0 + 1, c1>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            d = tx == c - K * T ? a[K][c] : d;
+            asm volatile("" : "+v"(d));   // a chain of selects, not an indexed load
+          });
+          dg[K] = d;
+          rinv[K] = recip_div64(d);
+        });
+        Real ysave[R], ny[R];
+        sfor<0, R>([&](auto Kc) {
+          ysave[decltype(Kc)::value] = y[decltype(Kc)::value][0];
+          ny[decltype(Kc)::value] = Real(0);
+        });
+        sfor<0, N>([&](auto ic) {
+          constexpr int k = N - 1 - decltype(ic)::value;
+          constexpr int kl = k % T;
+          constexpr int ks = k / T;
+          constexpr int SLK = kl % SL;
+          const double x = quot_div64(y[ks][0], a[ks][k], rinv[ks]);   // meaningful on lane kl
+          xr[ks] = tx == kl ? x : xr[ks];
+          ny[ks] = tx == kl ? y[ks][0] : ny[ks];
+          asm volatile("" : "+v"(xr[ks]), "+v"(ny[ks]));   // select now, not at the store
+          sfor<0, ks + 1>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            fnmac_bcast<T, SLK, K == 0>(y[K][0], x, a[K][k]);
+          });
+        });
+        bool miss = false;
+        sfor<0, R>([&](auto Kc) {
+          constexpr int K = decltype(Kc)::value;
+          miss |= (tx + K * T < N) & !quot_div64_exact(ny[K], dg[K], xr[K]);
+        });
+        if (__builtin_amdgcn_ballot_w64(miss) != 0) {
+          sfor<0, R>([&](auto Kc) { y[decltype(Kc)::value][0] = ysave[decltype(Kc)::value]; });
+          solve_divide();
+        }
+      } else {
+        solve_divide();
+      }
       bool bad = false;
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
