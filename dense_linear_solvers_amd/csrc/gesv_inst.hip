@@ -41,7 +41,7 @@ static int launch_kernel(void (*kernel)(P...), unsigned grid, unsigned threads, 
 template <typename Real, int N, int NRHS, int T, bool FACT>
 static int launch_panel(const LaunchPlan& p, const void* A, const void* B, void* X,
                         int32_t* piv, int32_t* info, hipStream_t stream) {
-  constexpr int PB = panel_width(N, NRHS, sizeof(Real) == 8);
+  constexpr int PB = panel_width(N, NRHS, sizeof(Real) == 8, T, FACT);
   using S = PanelShape<Real, N, NRHS, T, PB>;
   static_assert(S::BLOCK_BYTES == gesv_lds_bytes(N, NRHS, T, sizeof(Real) == 8),
                 "host and device LDS sizes disagree");

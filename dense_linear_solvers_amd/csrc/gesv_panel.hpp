@@ -133,7 +133,7 @@ struct PanelShape {
   // sides by position, then over them the packed upper triangle of U, row q
   // holding columns q..N-1); the group's LDS area, lu_group_elems
   static constexpr bool REG_SOLVE = lu_solve_in_registers(NRHS, T);
-  static_assert(B == panel_width(N, NRHS, sizeof(Real) == 8), "panel width");
+  static_assert(B <= kPanelMax && B <= N, "records sized for the widest panel");
   static constexpr int GROUP_ELEMS = lu_group_elems(N, NRHS, T, sizeof(Real) == 8);
   static constexpr int WAVE_BYTES = G * GROUP_ELEMS * (int)sizeof(Real);
   static constexpr int BLOCK_BYTES = kWavesPerBlock * WAVE_BYTES;
@@ -617,10 +617,14 @@ __device__ __forceinline__ bool upper_solve_store(Real* ut, int tx, int gbase, b
 // must be 1 and Bm is not read), X receives the factors in the layout of A:
 // LAPACK's row order, unit-lower L below the diagonal and U on and above it.
 template <typename Real, int N, int NRHS, int T, int B, bool FACT = false>
-__global__ void __launch_bounds__(kWaveSize* kWavesPerBlock)
+__global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
+                                  lu_min_waves(N, NRHS, sizeof(Real) == 8, T, FACT) > 0
+                                      ? lu_min_waves(N, NRHS, sizeof(Real) == 8, T, FACT)
+                                      : 1)
     gesv_panel_kernel(int col, int n, int nrhs, int64_t batch, const Real* __restrict__ A,
                       const Real* __restrict__ Bm, Real* __restrict__ X, int32_t* __restrict__ piv,
                       int32_t* __restrict__ info, uint32_t flags, int64_t ilv) {
+  static_assert(B == panel_width(N, NRHS, sizeof(Real) == 8, T, FACT), "panel width");
   static_assert(!FACT || NRHS == 1, "the factorization runs with one (unused) right-hand side");
   static_assert(N > B, "the first panel has trailing columns (input check)");
   using S = PanelShape<Real, N, NRHS, T, B>;

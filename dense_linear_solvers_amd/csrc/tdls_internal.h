@@ -124,10 +124,42 @@ constexpr bool lu_prefers_wider(int op, int N, bool is64, int T0, int T1) {
   return !is64 && N == 24 && op == kOpGetrs;
 }
 
+// LU solves (gesv) whose registers, with panels of two columns instead of
+// four, fit one more wave per SIMD, and that wave count, which the kernel
+// declares as its minimum occupancy (0: panels of four, no declaration).
+// Two columns halve the pivot-row entries and multipliers a step holds in
+// registers; the records are exchanged twice as often, which costs more
+// than it gives at the same occupancy (n = 32 float64: 0.887 -> 0.923 ms).
+// Measured against panels of four (HIP events, 262,144 row-major systems
+// unless stated; VGPRs before -> after):
+//   float64 n = 32, 1 rhs, 16 lanes: 203 -> 168 (4 spilled), 2 -> 3 waves,
+//     0.780 -> 0.753 ms (column-major headline shape);
+//   float64 n = 24, 16 lanes: 1 rhs 171 -> 143, 0.587 -> 0.559 ms; 2 rhs
+//     177 -> 149, 0.655 -> 0.622 ms; 4 rhs 187 -> 157, 0.702 -> 0.664 ms;
+//   float64 n = 48, 64 lanes (131,072 systems): 4 rhs 169 -> 145, 1.690 ->
+//     1.608 ms; 8 rhs 181 -> 153, 1.845 -> 1.788 ms;
+//   float32 n = 32, 8 rhs, 16 lanes: 129 -> 113, 3 -> 4 waves, 0.675 ->
+//     0.662 ms.
+// Not taken: getrf (n = 32 float64 spills 14 at three waves, 0.895 -> 0.927
+// ms; n = 24 even), float32 n = 16 quads with 2 or 4 rhs (even or slower),
+// float64 n = 8 quads with 8 rhs (a fourth wave spills 35 registers: 0.432
+// -> 0.549 ms).
+constexpr int lu_min_waves(int N, int NRHS, bool is64, int T, bool fact) {
+  if (fact) return 0;
+  if (is64 && N == 32 && NRHS == 1 && T == 16) return 3;
+  if (is64 && N == 24 && NRHS <= 4 && T == 16) return 3;
+  if (is64 && N == 48 && NRHS >= 4 && T == 64) return 3;
+  if (!is64 && N == 32 && NRHS == 8 && T == 16) return 4;
+  return 0;
+}
+
 // Panel width of the factorization (columns whose pivot rows are exchanged
-// together through LDS).
-constexpr int panel_width(int N, [[maybe_unused]] int NRHS, [[maybe_unused]] bool is64) {
-  return N < 4 ? N : 4;
+// together through LDS): kPanelMax, or 2 where that gives another wave per
+// SIMD (lu_min_waves).
+constexpr int kPanelMax = 4;
+constexpr int panel_width(int N, int NRHS, bool is64, int T, bool fact) {
+  if (N < kPanelMax) return N;
+  return lu_min_waves(N, NRHS, is64, T, fact) > 0 ? 2 : kPanelMax;
 }
 
 // The LU solve keeps U in registers for the back substitution when one
@@ -153,7 +185,7 @@ constexpr int lu_group_elems(int N, int NRHS, int T, bool is64) {
   const int es = is64 ? 8 : 4;
   const int vec = 16 / es;
   const int stride = (N + NRHS + vec - 1) / vec * vec;
-  const int B = panel_width(N, NRHS, is64);
+  const int B = N < kPanelMax ? N : kPanelMax;   // records of the widest panel
   const int rec = B * stride;
   if (lu_solve_in_registers(NRHS, T)) {
     const int budget = kLuLdsPerWave / (kWaveSize / T) / es / vec * vec;
