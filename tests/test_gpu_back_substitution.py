@@ -1,8 +1,10 @@
-"""GPU: the float64 back substitution from registers (one right-hand side,
-4- and 16-lane groups) forms each x_k from a reciprocal of U(k,k) made
-before the chain and checks afterwards that this was the division
-sequence's own result, solving again by division where it was not.  Both
-routes must give the oracle's IEEE quotients bit for bit.
+"""GPU: the float64 back substitution.  From registers (one right-hand
+side, 4- and 16-lane groups) it forms each x_k from a reciprocal of U(k,k)
+made before the chain and checks afterwards that this was the division
+sequence's own result, solving again by division where it was not; whole-
+wave groups (n = 32 at small batches forced here, n = 64) divide with U
+read from the packed LDS triangle.  Every route must give the oracle's
+IEEE quotients bit for bit.
 
 Inputs: well-conditioned random systems (the shortcut holds), and the same
 systems with right-hand sides of 2^-1000 and exactly zero (numerators the
@@ -72,7 +74,7 @@ def _systems(n, seed):
 
 
 @pytest.mark.parametrize("layout", ["row", "col"])
-@pytest.mark.parametrize("n", [5, 8, 16, 24, 32])
+@pytest.mark.parametrize("n", [5, 8, 16, 24, 32, 64])
 def test_back_substitution_quotients(n, layout, monkeypatch):
     A, B = _systems(n, 300 + n)
     A_st = oracle.to_storage(A, layout)
