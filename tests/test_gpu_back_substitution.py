@@ -2,7 +2,7 @@
 side, 4- and 16-lane groups) it forms each x_k from a reciprocal of U(k,k)
 made before the chain and checks afterwards that this was the division
 sequence's own result, solving again by division where it was not; whole-
-wave groups (n = 32 at small batches forced here, n = 64) divide with U
+wave groups (n = 24 and 32 when forced to them here, n = 64) divide with U
 read from the packed LDS triangle.  Every route must give the oracle's
 IEEE quotients bit for bit.
 
