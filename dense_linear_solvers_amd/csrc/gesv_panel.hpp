@@ -1159,6 +1159,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
   });
 
   const bool nf = pz != pz;   // a pivot was an infinity or a NaN
+  // The system index again, from the wave's first system and a lane index
+  // read anew: kept from the load, it held a register pair through the
+  // whole factorization (the compiler spilled it at three waves per SIMD).
+  int lane_e = (int)threadIdx.x & (kWaveSize - 1);
+  asm("" : "+v"(lane_e));
+  const int64_t sys_e = wave_first + lane_e / T;
+  const bool live_e = sys_e < batch;
 
   if constexpr (FACT) {
     // ---- factors: every row, whatever lane holds it, is row lab of L\U
@@ -1188,9 +1195,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
       if (group_any<T>(bad, gbase) && status == 0) status = -3;
     }
     const bool failed = status != 0;
-    if (live) {
-      Real* LUs = X + sys_start(sys, ilv, (int64_t)n * n);
-      int32_t* Ps = piv + sys_start(sys, ilv, n);
+    if (live_e) {
+      Real* LUs = X + sys_start(sys_e, ilv, (int64_t)n * n);
+      int32_t* Ps = piv + sys_start(sys_e, ilv, n);
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = lab[K];
@@ -1226,13 +1233,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
         const int qf = tx + K * T;
         if (qf < n) Ps[qf * ilv] = failed ? -1 : pv[K];
       });
-      if (tx == 0) info[sys] = status;
+      if (tx == 0) info[sys_e] = status;
     }
   } else {
     // ---- back substitution (see upper_solve_store): every row, whatever lane
     // holds it, stores its right-hand sides and then its U entries (columns
     // from its position on) by position
-    int32_t* Ps = piv + sys_start(live ? sys : 0, ilv, n);
+    int32_t* Ps = piv + sys_start(live_e ? sys_e : 0, ilv, n);
     wave_sync_lds();  // the last records have been read
     bool xbad;
     if constexpr (S::REG_SOLVE) {
@@ -1350,9 +1357,9 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
         bad |= (tx + K * T < n) & not_finite(xr[K]);
       });
       xbad = group_any<T>(bad, gbase);
-      if (live) {
+      if (live_e) {
         const bool zero = status != 0 || nf || xbad;
-        Real* Xs = X + sys_start(sys, ilv, (int64_t)n * nrhs);
+        Real* Xs = X + sys_start(sys_e, ilv, (int64_t)n * nrhs);
         sfor<0, R>([&](auto Kc) {
           constexpr int K = decltype(Kc)::value;
           const int q = tx + K * T;
@@ -1361,7 +1368,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
       }
     } else
     xbad = upper_solve_store<Real, N, NRHS, T>(
-        rec, tx, gbase, live, status != 0 || nf, live ? sys : 0, n, nrhs, col, ilv, X,
+        rec, tx, gbase, live_e, status != 0 || nf, live_e ? sys_e : 0, n, nrhs, col, ilv, X,
         [&](Real* yt) {
           sfor<0, R>([&](auto Kc) {
             constexpr int K = decltype(Kc)::value;
@@ -1392,13 +1399,13 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
     const bool failed = status != 0;
 
     // ---- piv (all -1 for a failed system) and info
-    if (live) {
+    if (live_e) {
       sfor<0, R>([&](auto Kc) {
         constexpr int K = decltype(Kc)::value;
         const int q = tx + K * T;
         if (q < n) Ps[q * ilv] = failed ? -1 : pv[K];
       });
-      if (tx == 0) info[sys] = status;
+      if (tx == 0) info[sys_e] = status;
     }
   }
 }
