@@ -1159,13 +1159,14 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
   });
 
   const bool nf = pz != pz;   // a pivot was an infinity or a NaN
-  // The system index again, from the wave's first system and a lane index
-  // read anew: kept from the load, it held a register pair through the
-  // whole factorization (the compiler spilled it at three waves per SIMD).
+  // The system index and group base again, from the wave's first system
+  // and a lane index read anew: kept from the load, they held registers
+  // through the whole factorization (spilled at three waves per SIMD).
   int lane_e = (int)threadIdx.x & (kWaveSize - 1);
   asm("" : "+v"(lane_e));
   const int64_t sys_e = wave_first + lane_e / T;
   const bool live_e = sys_e < batch;
+  const int gbase_e = lane_e / T * T;   // the group's first lane, likewise
 
   if constexpr (FACT) {
     // ---- factors: every row, whatever lane holds it, is row lab of L\U
@@ -1192,7 +1193,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
           bad |= real & (c < n) & not_finite(a[K][c]);
         });
       });
-      if (group_any<T>(bad, gbase) && status == 0) status = -3;
+      if (group_any<T>(bad, gbase_e) && status == 0) status = -3;
     }
     const bool failed = status != 0;
     if (live_e) {
@@ -1356,7 +1357,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
         constexpr int K = decltype(Kc)::value;
         bad |= (tx + K * T < n) & not_finite(xr[K]);
       });
-      xbad = group_any<T>(bad, gbase);
+      xbad = group_any<T>(bad, gbase_e);
       if (live_e) {
         const bool zero = status != 0 || nf || xbad;
         Real* Xs = X + sys_start(sys_e, ilv, (int64_t)n * nrhs);
@@ -1368,7 +1369,7 @@ __global__ void __launch_bounds__(kWaveSize* kWavesPerBlock,
       }
     } else
     xbad = upper_solve_store<Real, N, NRHS, T>(
-        rec, tx, gbase, live_e, status != 0 || nf, live_e ? sys_e : 0, n, nrhs, col, ilv, X,
+        rec, tx, gbase_e, live_e, status != 0 || nf, live_e ? sys_e : 0, n, nrhs, col, ilv, X,
         [&](Real* yt) {
           sfor<0, R>([&](auto Kc) {
             constexpr int K = decltype(Kc)::value;
