@@ -541,7 +541,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the batched solver shards systems across GPUs "
-              "with no communication, and this build measures the one-GPU share.",
+              "with no communication, so one GPU's share is what it measures.",
               file=sys.stderr)
         sys.exit(2)
 
